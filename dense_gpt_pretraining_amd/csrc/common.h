@@ -1,0 +1,125 @@
+// Device-side helpers shared by every kernel of the library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nc {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ bf16 <-> fp32
+__device__ __forceinline__ float bf2f(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+// round to nearest, ties to even (inputs are finite)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t b = __float_as_uint(f);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return static_cast<bf16_t>(b >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// element traits: storage type T <-> fp32 arithmetic
+template <typename T> struct Elt;
+template <> struct Elt<float> {
+    static __device__ __forceinline__ float ld(const float* p) { return *p; }
+    static __device__ __forceinline__ void st(float* p, float v) { *p = v; }
+    static constexpr int kVec = 4;  // elements per 16-byte access
+};
+template <> struct Elt<bf16_t> {
+    static __device__ __forceinline__ float ld(const bf16_t* p) { return bf2f(*p); }
+    static __device__ __forceinline__ void st(bf16_t* p, float v) { *p = f2bf(v); }
+    static constexpr int kVec = 8;
+};
+
+// 16-byte vector load/store of kVec elements converted to/from fp32
+template <typename T>
+__device__ __forceinline__ void ld_vec(const T* p, float* out);
+template <>
+__device__ __forceinline__ void ld_vec<float>(const float* p, float* out) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void ld_vec<bf16_t>(const bf16_t* p, float* out) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf_lo(v.x); out[1] = bf_hi(v.x); out[2] = bf_lo(v.y); out[3] = bf_hi(v.y);
+    out[4] = bf_lo(v.z); out[5] = bf_hi(v.z); out[6] = bf_lo(v.w); out[7] = bf_hi(v.w);
+}
+template <typename T>
+__device__ __forceinline__ void st_vec(T* p, const float* in);
+template <>
+__device__ __forceinline__ void st_vec<float>(float* p, const float* in) {
+    *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+}
+template <>
+__device__ __forceinline__ void st_vec<bf16_t>(bf16_t* p, const float* in) {
+    uint4 v;
+    v.x = pack_bf2(in[0], in[1]); v.y = pack_bf2(in[2], in[3]);
+    v.z = pack_bf2(in[4], in[5]); v.w = pack_bf2(in[6], in[7]);
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+// sum over groups of `width` consecutive lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int width) {
+    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// block-wide sum for blockDim.x a multiple of 64 (<= 1024); `red` holds
+// blockDim.x/64 floats of shared memory.  Every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < nw; ++i) s += red[i];
+    return s;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = -INFINITY;
+    for (int i = 0; i < nw; ++i) s = fmaxf(s, red[i]);
+    return s;
+}
+
+// tanh from its Taylor series near 0 and from 1 - 2/(exp(2x)+1) elsewhere
+__device__ __forceinline__ float tanh_f(float x) {
+    float ax = fabsf(x);
+    if (ax < 0.125f) {
+        float x2 = x * x;
+        // x - x^3/3 + 2x^5/15 - 17x^7/315
+        return x * (1.f + x2 * (-1.f / 3.f + x2 * (2.f / 15.f + x2 * (-17.f / 315.f))));
+    }
+    float e = __expf(2.f * ax);
+    float t = 1.f - 2.f / (e + 1.f);
+    return copysignf(t, x);
+}
+
+__host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace nc

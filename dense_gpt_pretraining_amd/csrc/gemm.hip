@@ -1,0 +1,478 @@
+// GEMM family of the step: C[m][n] = sum_k A(m,k) B(n,k) with fp32
+// accumulation and a fused epilogue.  Every linear layer of the model is
+// bias-free (architecture list of the nanochat article), so each forward
+// projection is Y = X W^T, each data gradient dX = dY W and each weight
+// gradient dW = dY^T X; all three are this one contraction with the operands
+// read either along k ("k-major") or along m/n ("mn-major").
+//
+// bf16: CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16).  A 256-thread
+// workgroup owns a 256 (m) x 256 (n) output tile; each of its 4 waves owns a
+// 128 x 128 quadrant held as 4 x 4 accumulator blocks of 32 x 32 fp32.  The
+// k loop stages 256 x 64 tiles of both operands in LDS, double-buffered, with
+// an XOR swizzle of the 16-byte chunks of each row so that neither the
+// fragment reads (8 consecutive rows, same chunk) nor the transposing writes
+// (rows 8 apart, same chunk) collide in a bank group.  mn-major operands are
+// loaded as 8 x 8 element blocks and transposed in registers before the LDS
+// write, so the fragment reads are the same 16-byte reads for every layout.
+// The MFMA "A" side takes the n rows and the "B" side the m rows, which puts
+// 4 consecutive n of one row m in each lane's accumulator registers: the
+// epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
+//
+// fp32: a plain LDS-tiled SIMT kernel (64 x 64 tiles, 4 x 4 per thread).
+#include "kernels.h"
+
+namespace nc {
+
+namespace {
+
+struct EpiDev {
+    int mode;
+    const float* rowscale;
+    const void* aux;
+    int accumulate;
+};
+
+template <typename T>
+__device__ __forceinline__ float epi_value(const EpiDev& e, int64_t m, int64_t idx, float acc) {
+    switch (e.mode) {
+        case EPI_ROWSCALE: return e.rowscale[m] * acc;
+        case EPI_ROWSCALE_RELU2: {
+            const float u = fmaxf(e.rowscale[m] * acc, 0.f);
+            return u * u;
+        }
+        case EPI_RESID: return Elt<T>::ld(static_cast<const T*>(e.aux) + idx) + acc;
+        case EPI_RELU2_BWD:
+            return e.rowscale[m] * acc * 2.f * sqrtf(Elt<T>::ld(static_cast<const T*>(e.aux) + idx));
+        default: return acc;  // EPI_STORE_T
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_store1(const EpiDev& e, void* C, int64_t ldc, int64_t m,
+                                           int64_t n, float acc) {
+    const int64_t idx = m * ldc + n;
+    if (e.mode == EPI_STORE_F32) {
+        float* c = static_cast<float*>(C) + idx;
+        *c = e.accumulate ? *c + acc : acc;
+    } else {
+        Elt<T>::st(static_cast<T*>(C) + idx, epi_value<T>(e, m, idx, acc));
+    }
+}
+
+// ------------------------------------------------------------------ SIMT
+constexpr int kSB = 64, kSK = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_gemm_simt(int M, int N, int K, const T* __restrict__ A,
+                                                   int64_t lda, int ak, const T* __restrict__ B,
+                                                   int64_t ldb, int bk, void* C, int64_t ldc,
+                                                   EpiDev e) {
+    __shared__ float As[kSK][kSB + 4];
+    __shared__ float Bs[kSK][kSB + 4];
+    const int m0 = blockIdx.y * kSB, n0 = blockIdx.x * kSB;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += kSK) {
+        for (int i = threadIdx.x; i < kSB * kSK; i += 256) {
+            int r, kk;
+            if (ak) { r = i / kSK; kk = i % kSK; } else { kk = i / kSB; r = i % kSB; }
+            const int64_t m = m0 + r, k = k0 + kk;
+            float v = 0.f;
+            if (m < M && k < K) v = Elt<T>::ld(A + (ak ? m * lda + k : k * lda + m));
+            As[kk][r] = v;
+        }
+        for (int i = threadIdx.x; i < kSB * kSK; i += 256) {
+            int r, kk;
+            if (bk) { r = i / kSK; kk = i % kSK; } else { kk = i / kSB; r = i % kSB; }
+            const int64_t n = n0 + r, k = k0 + kk;
+            float v = 0.f;
+            if (n < N && k < K) v = Elt<T>::ld(B + (bk ? n * ldb + k : k * ldb + n));
+            Bs[kk][r] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kSK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + ty * 4 + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t n = n0 + tx * 4 + j;
+            if (n < N) epi_store1<T>(e, C, ldc, m, n, acc[i][j]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ MFMA (bf16)
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kTileElems = kTM * kTK;                 // one operand tile (256 rows x 64 k)
+constexpr int kLdsBytes = 2 /*buffers*/ * 2 /*operands*/ * kTileElems * 2 /*bytes*/;
+
+// element offset of 16-byte chunk `ch` (0..7) of row `row` in a swizzled tile
+__device__ __forceinline__ int swz(int row, int ch) {
+    return row * kTK + ((ch ^ ((row ^ (row >> 3)) & 7)) << 3);
+}
+
+// transpose an 8 x 8 block of 16-bit values: in[r] holds row r (8 elements,
+// 2 per dword); out[c] receives column c
+__device__ __forceinline__ void transpose8x8(const uint4* in, uint4* out) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int d = c >> 1;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t x = reinterpret_cast<const uint32_t*>(&in[2 * p])[d];
+            const uint32_t y = reinterpret_cast<const uint32_t*>(&in[2 * p + 1])[d];
+            w[p] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+        }
+        out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+// Global -> registers for one 256-row x 64-k operand tile.
+//   k-major: thread t loads rows (t>>3) + 32 i, chunk t&7   (i = 0..7)
+//   mn-major: thread t loads k rows 8 (t>>5) + i at row chunk t&31
+template <bool KMAJ>
+__device__ __forceinline__ void tile_load(const bf16_t* __restrict__ P, int64_t ld, int rows,
+                                          int K, int r0, int k0, uint4* reg) {
+    const int t = threadIdx.x;
+    if (KMAJ) {
+        const int ch = t & 7;
+        const int k = k0 + ch * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = r0 + (t >> 3) + 32 * i;
+            if (r < rows && k < K)
+                reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)r * ld + k);
+            else
+                reg[i] = make_uint4(0, 0, 0, 0);
+        }
+    } else {
+        const int r = r0 + (t & 31) * 8;
+        const int kb = k0 + (t >> 5) * 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = kb + i;
+            if (r < rows && k < K)
+                reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)k * ld + r);
+            else
+                reg[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+template <bool KMAJ>
+__device__ __forceinline__ void tile_store(bf16_t* __restrict__ S, const uint4* reg) {
+    const int t = threadIdx.x;
+    if (KMAJ) {
+        const int ch = t & 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = (t >> 3) + 32 * i;
+            *reinterpret_cast<uint4*>(S + swz(r, ch)) = reg[i];
+        }
+    } else {
+        uint4 tr[8];
+        transpose8x8(reg, tr);
+        const int ch = t >> 5;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int r = (t & 31) * 8 + c;
+            *reinterpret_cast<uint4*>(S + swz(r, ch)) = tr[c];
+        }
+    }
+}
+
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+    // consecutive workgroup ids land on different XCDs (round robin over 8);
+    // give each XCD a contiguous range of tiles so neighbours share its L2
+    if (total % 8 != 0) return pid;
+    return (pid % 8) * (total / 8) + pid / 8;
+}
+
+template <int MODE>
+__device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, int64_t m,
+                                         float v0, float v1, float v2, float v3) {
+    if (MODE == EPI_STORE_F32) {
+        float4* c = reinterpret_cast<float4*>(static_cast<float*>(C) + idx);
+        float4 o = make_float4(v0, v1, v2, v3);
+        if (e.accumulate) {
+            const float4 p = *c;
+            o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
+        }
+        *c = o;
+    } else {
+        float o[4] = {v0, v1, v2, v3};
+        if (MODE == EPI_RESID || MODE == EPI_RELU2_BWD) {
+            const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(e.aux) + idx);
+            const float x[4] = {bf_lo(a.x), bf_hi(a.x), bf_lo(a.y), bf_hi(a.y)};
+            if (MODE == EPI_RESID) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] += x[q];
+            } else {
+                const float rs = 2.f * e.rowscale[m];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] *= rs * sqrtf(x[q]);
+            }
+        } else if (MODE == EPI_ROWSCALE) {
+            const float rs = e.rowscale[m];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] *= rs;
+        } else if (MODE == EPI_ROWSCALE_RELU2) {
+            const float rs = e.rowscale[m];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float u = fmaxf(rs * o[q], 0.f);
+                o[q] = u * u;
+            }
+        }
+        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(C) + idx) =
+            make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+    }
+}
+
+template <bool AK, bool BK, int MODE>
+__global__ __launch_bounds__(256, 1) void k_gemm_mfma(int M, int N, int K, int k_per_split,
+                                                      const bf16_t* __restrict__ A, int64_t lda,
+                                                      const bf16_t* __restrict__ B, int64_t ldb,
+                                                      void* C, int64_t ldc, EpiDev e,
+                                                      int64_t split_stride) {
+    extern __shared__ __align__(16) unsigned char lds_raw[];
+    bf16_t* lds = reinterpret_cast<bf16_t*>(lds_raw);
+
+    const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
+    const int total = tiles_m * tiles_n;
+    const int pid = xcd_remap(blockIdx.x, total);
+    // grouped order: 8 m-tiles share a column sweep over n
+    constexpr int kGroup = 8;
+    const int group = pid / (kGroup * tiles_n);
+    const int first_m = group * kGroup;
+    const int gsize = min(tiles_m - first_m, kGroup);
+    const int tm = first_m + (pid % (kGroup * tiles_n)) % gsize;
+    const int tn = (pid % (kGroup * tiles_n)) / gsize;
+    const int m0 = tm * kTM, n0 = tn * kTN;
+
+    const int kb = blockIdx.z * k_per_split;
+    const int ke = min(K, kb + k_per_split);
+    if (e.mode == EPI_STORE_F32 && split_stride) C = static_cast<float*>(C) + blockIdx.z * split_stride;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    uint4 ra[8], rb[8];
+    const int nk = (ke - kb + kTK - 1) / kTK;
+    if (nk > 0) {
+        tile_load<AK>(A, lda, M, ke, m0, kb, ra);
+        tile_load<BK>(B, ldb, N, ke, n0, kb, rb);
+        tile_store<AK>(lds, ra);
+        tile_store<BK>(lds + kTileElems, rb);
+    }
+    __syncthreads();
+
+    const int frow = lane & 31, fch = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int k0 = kb + (kt + 1) * kTK;
+            tile_load<AK>(A, lda, M, ke, m0, k0, ra);
+            tile_load<BK>(B, ldb, N, ke, n0, k0, rb);
+        }
+        const bf16_t* sA = lds + cur * 2 * kTileElems;
+        const bf16_t* sB = sA + kTileElems;
+#pragma unroll
+        for (int ks = 0; ks < kTK / 16; ++ks) {
+            bf16x8_t fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rn = wn * 128 + i * 32 + frow;
+                const uint4 v = *reinterpret_cast<const uint4*>(sB + swz(rn, 2 * ks + fch));
+                fa[i] = __builtin_bit_cast(bf16x8_t, v);
+                const int rm = wm * 128 + i * 32 + frow;
+                const uint4 w = *reinterpret_cast<const uint4*>(sA + swz(rm, 2 * ks + fch));
+                fb[i] = __builtin_bit_cast(bf16x8_t, w);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            bf16_t* nA = lds + (cur ^ 1) * 2 * kTileElems;
+            tile_store<AK>(nA, ra);
+            tile_store<BK>(nA + kTileElems, rb);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: lane holds m = m0 + wm*128 + 32 j + (lane & 31) and, for
+    // register group g, n = n0 + wn*128 + 32 i + 8 g + 4 (lane >> 5) + 0..3
+    const bool full_n = n0 + kTN <= N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t m = m0 + wm * 128 + 32 * j + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = n0 + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+                const float a[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                    acc[i][j][4 * g + 3]};
+                if (full_n || n + 3 < N) {
+                    epi_vec4<MODE>(e, C, m * ldc + n, m, a[0], a[1], a[2], a[3]);
+                } else {
+                    for (int q = 0; q < 4; ++q)
+                        if (n + q < N) epi_store1<bf16_t>(e, C, ldc, m, n + q, a[q]);
+                }
+            }
+        }
+    }
+}
+
+// out[m][n] = (accumulate ? out[m][n] : 0) + sum_s part[s][m][n], s in order;
+// partials have row stride ldp
+__global__ void k_splitk_reduce(const float* __restrict__ part, int splits, int M, int N,
+                                int64_t ldp, float* __restrict__ out, int64_t ldc, int accumulate) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * N) return;
+    const int64_t m = i / N, n = i % N;
+    float s = accumulate ? out[m * ldc + n] : 0.f;
+    for (int p = 0; p < splits; ++p) s += part[((int64_t)p * M + m) * ldp + n];
+    out[m * ldc + n] = s;
+}
+
+int choose_splits(int M, int N, int K) {
+    const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
+    int splits = 1;
+    // aim for at least 2 workgroups per compute unit (256 CUs) while each
+    // split keeps >= 1024 of k
+    while (tiles * splits < 512 && K / (splits * 2) >= 1024) splits *= 2;
+    return splits;
+}
+
+template <bool AK, bool BK, int MODE>
+hipError_t launch_mfma(int M, int N, int K, const bf16_t* A, int64_t lda, const bf16_t* B,
+                       int64_t ldb, void* C, int64_t ldc, const EpiDev& e, int splits,
+                       int64_t split_stride, hipStream_t s) {
+    auto kern = k_gemm_mfma<AK, BK, MODE>;
+    // allow more than 64 KiB of dynamic LDS (set once per process; idempotent)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    int k_per = (int)ceil_div(K, splits);
+    k_per = (int)ceil_div(k_per, kTK) * kTK;
+    const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
+    hipLaunchKernelGGL(kern, dim3(tiles, 1, splits), dim3(256), kLdsBytes, s, M, N, K, k_per, A,
+                       lda, B, ldb, C, ldc, e, split_stride);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// partial sums of a k-split keep rows 16-byte aligned
+int64_t splitk_ld(int N) { return (int64_t)ceil_div(N, 4) * 4; }
+
+size_t gemm_splitk_bytes(int M, int N, int K) {
+    const int splits = choose_splits(M, N, K);
+    return splits > 1 ? (size_t)splits * M * splitk_ld(N) * sizeof(float) : 0;
+}
+
+template <>
+hipError_t gemm<float>(int M, int N, int K, const float* A, int64_t lda, bool a_kmajor,
+                       const float* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
+                       const Epilogue& epi, float*, size_t, hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    EpiDev e{epi.mode, epi.rowscale, epi.aux, epi.accumulate ? 1 : 0};
+    dim3 grid((unsigned)ceil_div(N, kSB), (unsigned)ceil_div(M, kSB));
+    hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, s, M, N, K, A, lda,
+                       a_kmajor ? 1 : 0, B, ldb, b_kmajor ? 1 : 0, C, ldc, e);
+    return hipGetLastError();
+}
+
+template <>
+hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool a_kmajor,
+                        const bf16_t* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
+                        const Epilogue& epi, float* splitk_ws, size_t splitk_ws_bytes,
+                        hipStream_t s) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    EpiDev e{epi.mode, epi.rowscale, epi.aux, epi.accumulate ? 1 : 0};
+    int splits = 1;
+    if (epi.mode == EPI_STORE_F32) {
+        splits = choose_splits(M, N, K);
+        if (gemm_splitk_bytes(M, N, K) > splitk_ws_bytes || splitk_ws == nullptr) splits = 1;
+    }
+    // the epilogue's vector stores need 16-byte aligned rows
+    if (ldc % 4) return hipErrorInvalidValue;
+    void* out = C;
+    int64_t ld_out = ldc, stride = 0;
+    EpiDev ek = e;
+    if (splits > 1) {
+        out = splitk_ws;
+        ld_out = splitk_ld(N);
+        stride = (int64_t)M * ld_out;
+        ek.accumulate = 0;
+    }
+    hipError_t err;
+    if (a_kmajor && b_kmajor) {
+        switch (epi.mode) {
+            case EPI_STORE_F32:
+                err = launch_mfma<true, true, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_ROWSCALE:
+                err = launch_mfma<true, true, EPI_ROWSCALE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_ROWSCALE_RELU2:
+                err = launch_mfma<true, true, EPI_ROWSCALE_RELU2>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_RESID:
+                err = launch_mfma<true, true, EPI_RESID>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_RELU2_BWD:
+                err = launch_mfma<true, true, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_STORE_T:
+                err = launch_mfma<true, true, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (!a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
+        err = launch_mfma<false, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+    } else {
+        return hipErrorInvalidValue;  // layout/epilogue pair the step never uses
+    }
+    if (err != hipSuccess || splits == 1) return err;
+    const int64_t n = (int64_t)M * N;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
+                       splitk_ws, splits, M, N, splitk_ld(N), static_cast<float*>(C), ldc,
+                       e.accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace nc

@@ -1,0 +1,132 @@
+// Host-side launchers of the library's HIP kernels (internal interface between
+// the step runtime and the kernel files; not part of the C ABI).
+//
+// Every launcher enqueues on `s` and returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace nc {
+
+// ----------------------------------------------------------------- GEMM
+// C[m][n] = sum_k A(m,k) * B(n,k), fp32 accumulation, followed by an epilogue.
+//   A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B(n,k) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+enum EpiMode : int {
+    EPI_STORE_F32 = 0,   // Cf[m][n] = acc (+ Cf[m][n] if accumulate)
+    EPI_ROWSCALE = 1,    // C[m][n] = rowscale[m] * acc
+    EPI_ROWSCALE_RELU2 = 2,  // C[m][n] = relu(rowscale[m] * acc)^2
+    EPI_RESID = 3,       // C[m][n] = resid[m][n] + acc   (resid: T, ld = ldc)
+    EPI_RELU2_BWD = 4,   // C[m][n] = rowscale[m] * acc * 2*sqrt(aux[m][n]) (aux: T, ld = ldc)
+    EPI_STORE_T = 5,     // C[m][n] = acc, stored as T
+};
+struct Epilogue {
+    int mode = EPI_STORE_F32;
+    const float* rowscale = nullptr;
+    const void* aux = nullptr;   // resid or g, element type T, same ld as C
+    bool accumulate = false;     // EPI_STORE_F32 only
+};
+
+template <typename T>
+hipError_t gemm(int M, int N, int K, const T* A, int64_t lda, bool a_kmajor,
+                const T* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
+                const Epilogue& epi, float* splitk_ws, size_t splitk_ws_bytes,
+                hipStream_t s);
+// bytes of split-K scratch gemm() may use for an fp32 output of M x N
+size_t gemm_splitk_bytes(int M, int N, int K);
+
+// ----------------------------------------------------------------- attention
+// Per-row reference kernels (any T) and the dispatchers below.
+template <typename T>
+hipError_t attn_fwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_t ldkv, T* o,
+                         float* lse, int B, int Tn, int H, int hd, hipStream_t s);
+template <typename T>
+hipError_t attn_bwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_t ldkv,
+                         const T* o, const T* dout, const float* lse, float* delta, float* dq,
+                         float* dk, float* dv, int B, int Tn, int H, int hd, hipStream_t s);
+template <typename T>
+hipError_t attn_delta(const T* o, const T* dout, int64_t rows, int hd, float* delta,
+                      hipStream_t s);
+// Causal multi-query attention of B sequences of length T with H query heads
+// of width hd and one K/V head.  q: [B*T, H, hd] with token stride ldq;
+// k, v: [B*T, hd] with token stride ldkv; o: [B*T, H*hd]; lse: [B*T*H] fp32.
+template <typename T>
+hipError_t attn_fwd(const T* q, const T* k, const T* v, int64_t ldq,
+                    int64_t ldkv, T* o, float* lse, int B, int Tn, int H,
+                    int hd, hipStream_t s);
+// Backward: dq [B*T, H, hd], dk, dv [B*T, hd], all fp32; delta is scratch of
+// B*T*H floats.
+template <typename T>
+hipError_t attn_bwd(const T* q, const T* k, const T* v, int64_t ldq,
+                    int64_t ldkv, const T* o, const T* dout, const float* lse,
+                    float* delta, float* dq, float* dk, float* dv, int B,
+                    int Tn, int H, int hd, hipStream_t s);
+
+// ----------------------------------------------------------------- row kernels
+template <typename T>
+hipError_t embed_fwd(const T* wte, const int32_t* tok, int N, int D, float eps,
+                     T* out, float* r, hipStream_t s);
+template <typename T>
+hipError_t rms_stats(const T* x, int N, int D, float eps, float* r, hipStream_t s);
+hipError_t rope_tables(int Tn, int hd, float base, float* cos_t, float* sin_t,
+                       hipStream_t s);
+// in place on qkv [N, (H+2)*hd]: heads 0..H-1 (q) and H (k) are rotated and
+// normalised; rqk [N, H+1] receives the norm scales.
+template <typename T>
+hipError_t rope_qknorm_fwd(T* qkv, int N, int Tn, int H, int hd,
+                           const float* cos_t, const float* sin_t, float eps,
+                           float* rqk, hipStream_t s);
+// dqkv[N, (H+2)*hd] = r1[t] * d(pre-rotary q, k, v) from the attention-input
+// gradients dq [N,H,hd], dk, dv [N,hd] (fp32) and the saved normalised q, k.
+template <typename T>
+hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk,
+                           const float* dv, const float* rqk, const float* r1,
+                           int N, int Tn, int H, int hd, const float* cos_t,
+                           const float* sin_t, T* dqkv, hipStream_t s);
+// dres += dn - r^2 * x * mean(dn * x) over each row; dres_t = (T)dres
+template <typename T>
+hipError_t norm_bwd_resid(const float* dn, const T* x, const float* r, int N,
+                          int D, float* dres, T* dres_t, hipStream_t s);
+// de[t] = r0[t]*dh[t] - r0[t]^3 * e[t] * mean(dh[t]*e[t]), e[t] = wte[tok[t]]
+template <typename T>
+hipError_t embed_bwd_rows(const float* dh, const T* wte, const int32_t* tok,
+                          const float* r0, int N, int D, float* de, hipStream_t s);
+// Softcap + cross-entropy over rows of z [N, ldz] (V valid columns).
+// tok_loss[t] = logsumexp(c) - c[y]; if want_grad, z is overwritten by
+// rowscale[t] * inv_n * (softmax(c) - onehot(y)) * (1 - (c/s)^2), and the
+// padding columns V..ldz-1 by zeros.
+template <typename T>
+hipError_t softcap_ce(T* z, int64_t ldz, int V, int N, const int32_t* tgt,
+                      float cap, const float* rowscale, float inv_n,
+                      float* tok_loss, bool want_grad, hipStream_t s);
+// loss = mean(tok_loss[0..N-1]) (fixed summation order)
+hipError_t mean_reduce(const float* x, int N, float* out, hipStream_t s);
+// out[c][r] = in[r][c] for a rows x cols matrix; out row stride ld_out;
+// columns of out beyond `rows` up to ld_out are zero-filled.
+template <typename T>
+hipError_t transpose(const T* in, int rows, int cols, int64_t ld_in, T* out,
+                     int64_t ld_out, hipStream_t s);
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// ----------------------------------------------------------------- embedding grad
+// Deterministic scatter-add of de rows into dwte (fully overwritten):
+// dwte[v] = sum over t with tok[t] == v of de[t], summed in position order.
+size_t embed_grad_ws_bytes(int N, int D, int V);
+hipError_t embed_grad(const float* de, const int32_t* tok, int N, int D, int V,
+                      float* dwte, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ----------------------------------------------------------------- misc
+template <typename T>
+hipError_t init_normal(T* p, int64_t n, float std, uint64_t seed,
+                       uint64_t stream_id, hipStream_t s);
+template <typename T>
+hipError_t zero_elems(T* p, int64_t n, hipStream_t s);
+// records the HIP error behind an NC_ERR_HIP return (read by nc_last_hip_error)
+void note_hip_error(int err);
+hipError_t count_bad_ids(const int32_t* a, const int32_t* b, int64_t n, int V,
+                         int32_t* n_bad, hipStream_t s);
+
+}  // namespace nc

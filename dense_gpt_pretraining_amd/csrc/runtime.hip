@@ -1,0 +1,487 @@
+// Host runtime behind the C ABI of include/nc.h: configuration checks, the
+// parameter layout, the workspace plan and the launch sequence of one
+// forward(+backward) step on one stream.
+//
+// Step (nanochat article on vpshk.cn, architecture list; pre-norm placement is
+// the Llama-like reading): h0 = n(W_te[x]); per block
+//   a = n(h); [q;k;v] = a W_qkv^T; q,k rotated then normalised per head;
+//   h' = h + attn(q,k,v) W_o^T; m = n(h'); h'' = h' + relu(m W_fc^T)^2 W_proj^T;
+// then f = n(h_L), z = f W_lm^T, c = s tanh(z/s), loss = mean(lse(c) - c[y]).
+//
+// Parameter-free RMSNorm makes n(x) W^T = diag(r) (x W^T) with
+// r = 1/sqrt(mean(x^2) + eps), so no normalised copy of the residual stream
+// is ever stored: the norm enters the producing GEMM's epilogue as a row scale
+// r, and in the backward pass the same row scale is folded into the gradient
+// dy' = r dy.  Then dW = dy'^T x and, with dn' = dy' W, the input gradient is
+// dx = dn' - r^2 x mean(dn' * x).
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/nc.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kAlignElems = 128;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int vocab_pad(const nc_config& c) { return (int)round_up(c.vocab, 256); }
+
+int validate(const nc_config* c) {
+    if (!c) return NC_ERR_NULL;
+    if (c->dtype != NC_F32 && c->dtype != NC_BF16) return NC_ERR_DTYPE;
+    if (c->n_layer < 1 || c->d_model < 8 || c->n_head < 1 || c->d_mlp < 8 || c->vocab < 2 ||
+        c->seq_len < 1 || c->batch < 1 || c->n_kv_head < 1)
+        return NC_ERR_CONFIG;
+    if (!(c->softcap > 0.f) || !std::isfinite(c->softcap) || !(c->rms_eps >= 0.f) ||
+        !std::isfinite(c->rms_eps) || !(c->rope_base > 1.f) || !std::isfinite(c->rope_base))
+        return NC_ERR_CONFIG;
+    if (c->head_dim != 64 && c->head_dim != 128) return NC_ERR_UNSUPPORTED;
+    if (c->n_kv_head != 1) return NC_ERR_UNSUPPORTED;
+    if (c->d_model % 8 || c->d_mlp % 8) return NC_ERR_UNSUPPORTED;
+    if (c->seq_len % 64) return NC_ERR_UNSUPPORTED;
+    if (c->softcap > 60.f) return NC_ERR_UNSUPPORTED;
+    if (c->vocab > (1 << 24)) return NC_ERR_UNSUPPORTED;
+    // the fused cross-entropy keeps a padded vocabulary row in registers
+    const int64_t row_cap = (int64_t)32 * 256 * (c->dtype == NC_BF16 ? 8 : 4);
+    if (vocab_pad(*c) > row_cap) return NC_ERR_UNSUPPORTED;
+    const int64_t N = (int64_t)c->batch * c->seq_len;
+    if (N > (1 << 24)) return NC_ERR_UNSUPPORTED;
+    const int64_t widest = std::max<int64_t>(
+        {(int64_t)vocab_pad(*c), c->d_mlp, (int64_t)(c->n_head + 2) * c->head_dim, c->d_model});
+    if (N * widest >= ((int64_t)1 << 40)) return NC_ERR_UNSUPPORTED;
+    return NC_OK;
+}
+
+struct TensorDesc {
+    std::string name;
+    int64_t offset;
+    int32_t rows, cols;
+};
+
+// wq, wk, wv of a layer are adjacent with no padding between them so that
+// together they form one [(H+2) hd, D] matrix
+std::vector<TensorDesc> layout(const nc_config& c, int64_t* total) {
+    std::vector<TensorDesc> out;
+    const int D = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_mlp, V = c.vocab;
+    int64_t off = 0;
+    auto add = [&](const std::string& n, int r, int k, bool pad_after) {
+        out.push_back({n, off, r, k});
+        off += (int64_t)r * k;
+        if (pad_after) off = round_up(off, kAlignElems);
+    };
+    add("wte", V, D, true);
+    for (int l = 0; l < c.n_layer; ++l) {
+        const std::string p = "h" + std::to_string(l) + ".";
+        add(p + "wq", H * hd, D, false);
+        add(p + "wk", hd, D, false);
+        add(p + "wv", hd, D, true);
+        add(p + "wo", D, H * hd, true);
+        add(p + "wfc", F, D, true);
+        add(p + "wproj", D, F, true);
+    }
+    add("wlm", V, D, true);
+    if (total) *total = off;
+    return out;
+}
+
+// ------------------------------------------------------------------ workspace plan
+struct Plan {
+    // per-layer saved tensors: element offsets relative to buffer bases
+    size_t bytes = 0;
+    // offsets (bytes) of each region inside the workspace
+    size_t cos_t, sin_t, r0, x, r1, qkv, rqk, o, lse, xm, r2, g, rf, z, tok_loss, loss_tmp;
+    size_t dres, dres_t, dn, dgu, dout, delta, dq, dk, dv, dqkv, wt, splitk, embed;
+    size_t splitk_bytes = 0, embed_bytes = 0;
+    int slots = 1;     // saved-activation slots per layer tensor (L with backward, 1 without)
+    int x_slots = 2;   // block inputs: L+1 with backward, 2 (ping-pong) without
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(const nc_config& c, bool bwd) {
+    Plan p;
+    const int64_t N = (int64_t)c.batch * c.seq_len;
+    const int64_t D = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_mlp, V = c.vocab;
+    const int64_t Vp = vocab_pad(c);
+    const int64_t Wq = (H + 2) * hd;
+    const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+    const int L = c.n_layer;
+    p.slots = bwd ? L : 1;
+    p.x_slots = bwd ? L + 1 : 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t r = off; off += align256(bytes); return r; };
+    p.cos_t = take((size_t)c.seq_len * (hd / 2) * 4);
+    p.sin_t = take((size_t)c.seq_len * (hd / 2) * 4);
+    p.r0 = take((size_t)N * 4);
+    p.x = take((size_t)p.x_slots * align256(N * D * es));
+    p.r1 = take((size_t)p.slots * align256(N * 4));
+    p.qkv = take((size_t)p.slots * align256(N * Wq * es));
+    p.rqk = take((size_t)p.slots * align256(N * (H + 1) * 4));
+    p.o = take((size_t)p.slots * align256(N * H * hd * es));
+    p.lse = take((size_t)p.slots * align256(N * H * 4));
+    p.xm = take((size_t)p.slots * align256(N * D * es));
+    p.r2 = take((size_t)p.slots * align256(N * 4));
+    p.g = take((size_t)p.slots * align256(N * F * es));
+    p.rf = take((size_t)N * 4);
+    p.z = take((size_t)N * Vp * es);
+    p.tok_loss = take((size_t)N * 4);
+    p.loss_tmp = take(16);
+    if (bwd) {
+        p.dres = take((size_t)N * D * 4);
+        p.dres_t = take((size_t)N * D * es);
+        p.dn = take((size_t)N * D * 4);
+        p.dgu = take((size_t)N * F * es);
+        p.dout = take((size_t)N * H * hd * es);
+        p.delta = take((size_t)N * H * 4);
+        p.dq = take((size_t)N * H * hd * 4);
+        p.dk = take((size_t)N * hd * 4);
+        p.dv = take((size_t)N * hd * 4);
+        p.dqkv = take((size_t)N * Wq * es);
+        const int64_t wt_elems = std::max<int64_t>({D * Vp, D * F, D * Wq, H * hd * D});
+        p.wt = take((size_t)wt_elems * es);
+        size_t sk = 0;
+        sk = std::max(sk, nc::gemm_splitk_bytes((int)V, (int)D, (int)N));
+        sk = std::max(sk, nc::gemm_splitk_bytes((int)D, (int)F, (int)N));
+        sk = std::max(sk, nc::gemm_splitk_bytes((int)F, (int)D, (int)N));
+        sk = std::max(sk, nc::gemm_splitk_bytes((int)D, (int)(H * hd), (int)N));
+        sk = std::max(sk, nc::gemm_splitk_bytes((int)Wq, (int)D, (int)N));
+        p.splitk_bytes = sk;
+        p.splitk = take(sk);
+        p.embed_bytes = nc::embed_grad_ws_bytes((int)N, (int)D, (int)V);
+        p.embed = take(p.embed_bytes);
+    }
+    p.bytes = off;
+    return p;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define NC_TRY(expr)                                   \
+    do {                                               \
+        hipError_t e_ = (expr);                        \
+        if (e_ != hipSuccess) {                        \
+            g_last_hip_error = (int)e_;                \
+            return NC_ERR_HIP;                         \
+        }                                              \
+    } while (0)
+
+template <typename T>
+struct Step {
+    const nc_config& c;
+    const Plan& p;
+    char* ws;
+    hipStream_t s;
+    const T* params;
+    std::vector<TensorDesc> lay;
+    int64_t N, D, H, hd, F, V, Vp, Wq;
+
+    Step(const nc_config& cfg, const Plan& plan, void* w, hipStream_t st, const void* prm)
+        : c(cfg), p(plan), ws(static_cast<char*>(w)), s(st), params(static_cast<const T*>(prm)) {
+        lay = layout(c, nullptr);
+        N = (int64_t)c.batch * c.seq_len;
+        D = c.d_model; H = c.n_head; hd = c.head_dim; F = c.d_mlp; V = c.vocab;
+        Vp = vocab_pad(c);
+        Wq = (H + 2) * hd;
+    }
+    template <typename U> U* at(size_t off) { return reinterpret_cast<U*>(ws + off); }
+    template <typename U> U* slot(size_t base, int i, size_t per_bytes) {
+        return reinterpret_cast<U*>(ws + base + (size_t)i * align256(per_bytes));
+    }
+    const T* W(int idx) const { return params + lay[idx].offset; }
+    // tensor indices in the layout
+    int i_wte() const { return 0; }
+    int i_layer(int l, int k) const { return 1 + 6 * l + k; }  // k: 0 wq,1 wk,2 wv,3 wo,4 wfc,5 wproj
+    int i_wlm() const { return 1 + 6 * c.n_layer; }
+
+    size_t es() const { return sizeof(T); }
+    T* X(int i) { return slot<T>(p.x, i, N * D * es()); }
+    float* R1(int l) { return slot<float>(p.r1, l, N * 4); }
+    T* QKV(int l) { return slot<T>(p.qkv, l, N * Wq * es()); }
+    float* RQK(int l) { return slot<float>(p.rqk, l, N * (H + 1) * 4); }
+    T* O(int l) { return slot<T>(p.o, l, N * H * hd * es()); }
+    float* LSE(int l) { return slot<float>(p.lse, l, N * H * 4); }
+    T* XM(int l) { return slot<T>(p.xm, l, N * D * es()); }
+    float* R2(int l) { return slot<float>(p.r2, l, N * 4); }
+    T* G(int l) { return slot<T>(p.g, l, N * F * es()); }
+
+    nc::Epilogue epi(int mode, const float* rs = nullptr, const void* aux = nullptr) {
+        nc::Epilogue e;
+        e.mode = mode;
+        e.rowscale = rs;
+        e.aux = aux;
+        return e;
+    }
+
+    int forward(const int32_t* tok, const int32_t* tgt, float* loss, float* tok_loss, bool bwd) {
+        const float eps = c.rms_eps;
+        float* cos_t = at<float>(p.cos_t);
+        float* sin_t = at<float>(p.sin_t);
+        NC_TRY(nc::rope_tables(c.seq_len, (int)hd, c.rope_base, cos_t, sin_t, s));
+        NC_TRY(nc::embed_fwd<T>(W(i_wte()), tok, (int)N, (int)D, eps, X(0), at<float>(p.r0), s));
+        const int L = c.n_layer;
+        for (int l = 0; l < L; ++l) {
+            const int sl = bwd ? l : 0;
+            T* x = X(bwd ? l : (l & 1));
+            T* xn = X(bwd ? l + 1 : ((l + 1) & 1));
+            float* r1 = R1(sl);
+            T* qkv = QKV(sl);
+            NC_TRY(nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
+                               Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
+            NC_TRY(nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t, sin_t,
+                                          eps, RQK(sl), s));
+            NC_TRY(nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
+                                   c.batch, c.seq_len, (int)H, (int)hd, s));
+            T* xm = XM(sl);
+            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true, W(i_layer(l, 3)),
+                               H * hd, true, xm, D, epi(nc::EPI_RESID, nullptr, x), nullptr, 0, s));
+            float* r2 = R2(sl);
+            NC_TRY(nc::rms_stats<T>(xm, (int)N, (int)D, eps, r2, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)F, (int)D, xm, D, true, W(i_layer(l, 4)), D, true,
+                               G(sl), F, epi(nc::EPI_ROWSCALE_RELU2, r2), nullptr, 0, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)F, G(sl), F, true, W(i_layer(l, 5)), F, true,
+                               xn, D, epi(nc::EPI_RESID, nullptr, xm), nullptr, 0, s));
+        }
+        T* hL = X(bwd ? L : (L & 1));
+        float* rf = at<float>(p.rf);
+        NC_TRY(nc::rms_stats<T>(hL, (int)N, (int)D, eps, rf, s));
+        T* z = at<T>(p.z);
+        NC_TRY(nc::gemm<T>((int)N, (int)V, (int)D, hL, D, true, W(i_wlm()), D, true, z, Vp,
+                           epi(nc::EPI_ROWSCALE, rf), nullptr, 0, s));
+        float* tl = tok_loss ? tok_loss : at<float>(p.tok_loss);
+        NC_TRY(nc::softcap_ce<T>(z, Vp, (int)V, (int)N, tgt, c.softcap, rf, 1.f / (float)N, tl,
+                                 bwd, s));
+        NC_TRY(nc::mean_reduce(tl, (int)N, loss, s));
+        return NC_OK;
+    }
+
+    int backward(const int32_t* tok, float* grads) {
+        const int L = c.n_layer;
+        T* wt = at<T>(p.wt);
+        float* sk = at<float>(p.splitk);
+        const size_t skb = p.splitk_bytes;
+        float* dres = at<float>(p.dres);
+        T* dres_t = at<T>(p.dres_t);
+        float* dn = at<float>(p.dn);
+        T* z = at<T>(p.z);  // now holds r_f/N * dloss/dz
+        auto G_of = [&](int idx) { return grads + lay[idx].offset; };
+
+        // head: df' = dz' W_lm, dW_lm = dz'^T h_L
+        T* hL = X(L);
+        NC_TRY(nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
+        NC_TRY(nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
+                           epi(nc::EPI_STORE_F32), nullptr, 0, s));
+        NC_TRY(nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
+                           epi(nc::EPI_STORE_F32), sk, skb, s));
+        NC_TRY(nc::zero_elems<float>(dres, N * D, s));
+        NC_TRY(nc::norm_bwd_resid<T>(dn, hL, at<float>(p.rf), (int)N, (int)D, dres, dres_t, s));
+
+        T* dgu = at<T>(p.dgu);
+        T* dout = at<T>(p.dout);
+        T* dqkv = at<T>(p.dqkv);
+        float* dq = at<float>(p.dq);
+        float* dk = at<float>(p.dk);
+        float* dv = at<float>(p.dv);
+        const float* cos_t = at<float>(p.cos_t);
+        const float* sin_t = at<float>(p.sin_t);
+        for (int l = L - 1; l >= 0; --l) {
+            T* x = X(l);
+            T* xm = XM(l);
+            // MLP: x_{l+1} = xm + relu(r2 xm W_fc^T)^2 W_proj^T
+            NC_TRY(nc::transpose<T>(W(i_layer(l, 5)), (int)D, (int)F, F, wt, D, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)F, (int)D, dres_t, D, true, wt, D, true, dgu, F,
+                               epi(nc::EPI_RELU2_BWD, R2(l), G(l)), nullptr, 0, s));
+            NC_TRY(nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(l), F, false,
+                               G_of(i_layer(l, 5)), F, epi(nc::EPI_STORE_F32), sk, skb, s));
+            NC_TRY(nc::transpose<T>(W(i_layer(l, 4)), (int)F, (int)D, D, wt, F, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)F, dgu, F, true, wt, F, true, dn, D,
+                               epi(nc::EPI_STORE_F32), nullptr, 0, s));
+            NC_TRY(nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
+                               G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
+            NC_TRY(nc::norm_bwd_resid<T>(dn, xm, R2(l), (int)N, (int)D, dres, dres_t, s));
+            // attention: xm = x + o W_o^T
+            NC_TRY(nc::transpose<T>(W(i_layer(l, 3)), (int)D, (int)(H * hd), H * hd, wt, D, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)(H * hd), (int)D, dres_t, D, true, wt, D, true, dout,
+                               H * hd, epi(nc::EPI_STORE_T), nullptr, 0, s));
+            NC_TRY(nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(l), H * hd, false,
+                               G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb, s));
+            T* qkv = QKV(l);
+            NC_TRY(nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
+                                   LSE(l), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
+                                   (int)H, (int)hd, s));
+            NC_TRY(nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
+                                          (int)H, (int)hd, cos_t, sin_t, dqkv, s));
+            NC_TRY(nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
+            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)Wq, dqkv, Wq, true, wt, Wq, true, dn, D,
+                               epi(nc::EPI_STORE_F32), nullptr, 0, s));
+            NC_TRY(nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
+                               G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
+            NC_TRY(nc::norm_bwd_resid<T>(dn, x, R1(l), (int)N, (int)D, dres, dres_t, s));
+        }
+        // embedding: h0 = r0 e, e = W_te[tok]
+        float* de = dn;
+        NC_TRY(nc::embed_bwd_rows<T>(dres, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de, s));
+        NC_TRY(nc::embed_grad(de, tok, (int)N, (int)D, (int)V, G_of(i_wte()), ws + p.embed,
+                              p.embed_bytes, s));
+        return NC_OK;
+    }
+};
+
+template <typename T>
+int run_step(const nc_config& c, const void* params, const int32_t* tok, const int32_t* tgt,
+             float* loss, float* tok_loss, float* grads, void* ws, size_t ws_bytes,
+             hipStream_t s) {
+    const bool bwd = grads != nullptr;
+    Plan p = make_plan(c, bwd);
+    if (ws_bytes < p.bytes) return NC_ERR_WORKSPACE;
+    Step<T> st(c, p, ws, s, params);
+    int rc = st.forward(tok, tgt, loss, tok_loss, bwd);
+    if (rc != NC_OK || !bwd) return rc;
+    return st.backward(tok, grads);
+}
+
+int check_common(const nc_config* cfg, const void* params, const int32_t* tok,
+                 const int32_t* tgt, const float* loss, const float* tok_loss, const void* ws) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!params || !tok || !tgt || !loss || !ws) return NC_ERR_NULL;
+    if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(tok, 16) || !aligned(tgt, 16) ||
+        !aligned(loss, 4) || (tok_loss && !aligned(tok_loss, 16)))
+        return NC_ERR_ALIGN;
+    return NC_OK;
+}
+
+}  // namespace
+
+namespace nc {
+void note_hip_error(int err) { g_last_hip_error = err; }
+}  // namespace nc
+
+extern "C" {
+
+int nc_param_count(const nc_config* cfg, int64_t* n_elems) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!n_elems) return NC_ERR_NULL;
+    layout(*cfg, n_elems);
+    return NC_OK;
+}
+
+int nc_param_layout(const nc_config* cfg, nc_tensor_info* out, int32_t cap, int32_t* n_out) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!n_out) return NC_ERR_NULL;
+    std::vector<TensorDesc> lay = layout(*cfg, nullptr);
+    *n_out = (int32_t)lay.size();
+    if (cap < (int32_t)lay.size()) return NC_ERR_CAPACITY;
+    if (!out) return NC_ERR_NULL;
+    for (size_t i = 0; i < lay.size(); ++i) {
+        std::memset(out[i].name, 0, sizeof(out[i].name));
+        std::strncpy(out[i].name, lay[i].name.c_str(), sizeof(out[i].name) - 1);
+        out[i].offset = lay[i].offset;
+        out[i].rows = lay[i].rows;
+        out[i].cols = lay[i].cols;
+    }
+    return NC_OK;
+}
+
+int nc_workspace_size(const nc_config* cfg, int32_t with_backward, size_t* bytes) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!bytes) return NC_ERR_NULL;
+    *bytes = make_plan(*cfg, with_backward != 0).bytes;
+    return NC_OK;
+}
+
+int nc_init_params(const nc_config* cfg, uint64_t seed, void* params, void* stream) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!params) return NC_ERR_NULL;
+    if (!aligned(params, 256)) return NC_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int64_t total = 0;
+    std::vector<TensorDesc> lay = layout(*cfg, &total);
+    const bool bf = cfg->dtype == NC_BF16;
+    if (bf)
+        NC_TRY(nc::zero_elems<nc::bf16_t>(static_cast<nc::bf16_t*>(params), total, s));
+    else
+        NC_TRY(nc::zero_elems<float>(static_cast<float*>(params), total, s));
+    for (size_t i = 0; i < lay.size(); ++i) {
+        const float stdv = (lay[i].name == "wlm") ? 0.001f : 0.02f;
+        const int64_t n = (int64_t)lay[i].rows * lay[i].cols;
+        if (bf)
+            NC_TRY(nc::init_normal<nc::bf16_t>(static_cast<nc::bf16_t*>(params) + lay[i].offset, n,
+                                               stdv, seed, (uint64_t)i, s));
+        else
+            NC_TRY(nc::init_normal<float>(static_cast<float*>(params) + lay[i].offset, n, stdv,
+                                          seed, (uint64_t)i, s));
+    }
+    return NC_OK;
+}
+
+int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tokens,
+                    const int32_t* targets, float* loss, float* token_loss, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int rc = check_common(cfg, params, tokens, targets, loss, token_loss, ws);
+    if (rc != NC_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cfg->dtype == NC_BF16)
+        return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, token_loss, nullptr, ws,
+                                    ws_bytes, s);
+    return run_step<float>(*cfg, params, tokens, targets, loss, token_loss, nullptr, ws, ws_bytes,
+                           s);
+}
+
+int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t* tokens,
+                        const int32_t* targets, float* loss, float* token_loss, float* grads,
+                        void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_common(cfg, params, tokens, targets, loss, token_loss, ws);
+    if (rc != NC_OK) return rc;
+    if (!grads) return NC_ERR_NULL;
+    if (!aligned(grads, 256)) return NC_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cfg->dtype == NC_BF16)
+        return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, token_loss, grads, ws,
+                                    ws_bytes, s);
+    return run_step<float>(*cfg, params, tokens, targets, loss, token_loss, grads, ws, ws_bytes,
+                           s);
+}
+
+int nc_validate_tokens(const nc_config* cfg, const int32_t* tokens, const int32_t* targets,
+                       int32_t* n_bad, void* stream) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!tokens || !targets || !n_bad) return NC_ERR_NULL;
+    if (!aligned(tokens, 4) || !aligned(targets, 4) || !aligned(n_bad, 4)) return NC_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    NC_TRY(nc::zero_elems<int32_t>(n_bad, 1, s));
+    NC_TRY(nc::count_bad_ids(tokens, targets, (int64_t)cfg->batch * cfg->seq_len, cfg->vocab,
+                             n_bad, s));
+    return NC_OK;
+}
+
+const char* nc_status_string(int status) {
+    switch (status) {
+        case NC_OK: return "ok";
+        case NC_ERR_NULL: return "a required pointer is NULL";
+        case NC_ERR_CONFIG: return "a config field is out of range";
+        case NC_ERR_DTYPE: return "unknown dtype";
+        case NC_ERR_WORKSPACE: return "workspace smaller than nc_workspace_size";
+        case NC_ERR_ALIGN: return "a device pointer is not aligned";
+        case NC_ERR_HIP: return "a HIP call or kernel launch failed";
+        case NC_ERR_UNSUPPORTED: return "valid model, but a shape this build does not run";
+        case NC_ERR_CAPACITY: return "output array too small";
+        default: return "unknown status";
+    }
+}
+
+int nc_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+/*
+ * nc_ops.h -- unit-level entry points of the step library, one per kernel
+ * family, so that each piece of the step can be checked on its own against a
+ * CPU reference.  They run exactly the kernels nc_forward_backward runs.
+ *
+ * Conventions are those of nc.h: device pointers, caller-owned buffers,
+ * asynchronous on `stream` (a hipStream_t), host-side validation before any
+ * device work, NC_* status codes.  `dtype` is NC_F32 or NC_BF16 and gives the
+ * element type of every tensor documented as "T"; fp32 tensors are float.
+ * Every device pointer must be 16-byte aligned.
+ */
+#ifndef NC_OPS_H
+#define NC_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * C[m][n] = sum_k A(m,k) B(n,k), fp32 accumulation, C fp32 [M, N] row stride
+ * ldc.  A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m] (T), likewise B with
+ * b_kmajor.  This is the contraction of every bias-free linear layer (forward
+ * X W^T, data gradient dY W, weight gradient dY^T X).  bf16 supports the
+ * (k-major, k-major) and (mn-major, mn-major) pairs; K and both leading
+ * dimensions must be multiples of 8.  ws (may be NULL, ws_bytes 0) is scratch
+ * for a k-split; with too little scratch the k loop is not split.
+ */
+int nc_op_matmul(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, int64_t lda,
+                 int32_t a_kmajor, const void* B, int64_t ldb, int32_t b_kmajor, float* C,
+                 int64_t ldc, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Causal multi-query attention (one shared K/V head; architecture list of the
+ * nanochat article).  q: T [B*T, H, hd] with token stride ldq (elements);
+ * k, v: T [B*T, hd] with token stride ldkv; o: T [B*T, H*hd];
+ * lse: fp32 [B*T*H], the log-sum-exp of each row's scaled scores.
+ * o[t, j] = sum_{tau <= t} softmax(q[t,j].k[tau] / sqrt(hd)) v[tau].
+ * hd is 64 or 128, T a multiple of 64.
+ */
+int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
+                        const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
+                        void* o, float* lse, void* stream);
+
+/*
+ * Backward of nc_op_attention_fwd for output gradient dout (T [B*T, H*hd]).
+ * dq fp32 [B*T, H, hd]; dk, dv fp32 [B*T, hd]; delta: fp32 scratch [B*T*H].
+ */
+int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
+                        const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
+                        const void* o, const void* dout, const float* lse, float* delta,
+                        float* dq, float* dk, float* dv, void* stream);
+
+/*
+ * Softcap + cross-entropy over the rows of z (T [N, ldz], V valid columns,
+ * ldz a multiple of 8 and >= V): c = s tanh(z/s), tok_loss[t] =
+ * logsumexp(c_t) - c_t[y_t].  If want_grad, z is overwritten with
+ * rowscale[t] * inv_n * (softmax(c_t) - onehot(y_t)) * (1 - (c_t/s)^2) and the
+ * columns V..ldz-1 with zeros.  0 < s <= 60.
+ */
+int nc_op_softcap_ce(int32_t dtype, int32_t N, int32_t V, int64_t ldz, void* z,
+                     const int32_t* targets, float softcap, const float* rowscale, float inv_n,
+                     float* tok_loss, int32_t want_grad, void* stream);
+
+/*
+ * Rotary embedding then QK-norm, in place on qkv (T [B*T, (H+2)*hd]): the H
+ * query heads and the key head of each token are rotated (pair (i, i+hd/2) of
+ * position t by angle t*base^(-2i/hd)) and RMS-normalised; the value head is
+ * untouched.  rqk fp32 [B*T, H+1] receives 1/sqrt(mean(u^2)+eps) of each
+ * rotated head.  tables: fp32 scratch of T*hd floats.
+ */
+int nc_op_rope_qknorm_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd, void* qkv,
+                          float base, float eps, float* rqk, float* tables, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NC_OPS_H */

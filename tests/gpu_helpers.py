@@ -1,0 +1,52 @@
+"""Shared helpers of the GPU tests: device buffers from host arrays and the
+comparison metrics the parity bar is stated in."""
+import numpy as np
+
+from nc_synth import bf16_bits, bf16_round
+
+
+def require_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    return torch
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    """Host float array -> device tensor of the library's element type."""
+    import torch
+    if dtype == "bf16":
+        bits = bf16_bits(np.ascontiguousarray(a, dtype=np.float32))
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def from_dev(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        u = t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def rand(shape, seed, scale=1.0, dtype="bf16"):
+    a = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * np.float32(scale)
+    return bf16_round(a) if dtype == "bf16" else a
+
+
+def rel_l2(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    n = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (n if n > 0 else 1.0))
+
+
+def cosine(got, want):
+    got = np.asarray(got, dtype=np.float64).ravel()
+    want = np.asarray(want, dtype=np.float64).ravel()
+    d = np.linalg.norm(got) * np.linalg.norm(want)
+    return float(got @ want / d) if d > 0 else 1.0
+
+
+def stream():
+    import torch
+    return torch.cuda.current_stream().cuda_stream

@@ -1,0 +1,181 @@
+"""GPU parity of each kernel family against the oracle's primitives, through
+the unit-level C ABI (include/nc_ops.h).
+
+Tolerances come from the arithmetic: bf16 inputs are exact in both paths, the
+GPU accumulates in fp32 (relative error ~1e-6 here), and every bf16 output is
+rounded once (relative error <= 2^-9 per element, so rel-L2 a few 1e-3); the
+bar for a bf16 output is 1e-2 rel-L2, for an fp32 output of bf16 inputs 2e-5
+(matmul) and 1e-2 where an intermediate is rounded to bf16 first.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import from_dev, rand, rel_l2, require_gpu, stream, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": 0, "bf16": 1}
+
+
+def _b():
+    from dense_gpt_pretraining_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K,kmajor", [
+    (300, 520, 192, True),      # several 256 tiles, ragged m and n tails
+    (256, 256, 64, True),       # exactly one tile
+    (1, 8, 8, True),            # degenerate
+    (264, 136, 1000, False),    # mn-major operands (weight-gradient layout), ragged k
+    (512, 768, 4096, False),    # long k: split over the k loop
+])
+def test_matmul(dtype, M, N, K, kmajor):
+    torch = require_gpu()
+    b = _b()
+    A = rand((M, K), 1, dtype=dtype)
+    B = rand((N, K), 2, dtype=dtype)
+    want = A.astype(np.float64) @ B.astype(np.float64).T
+    if kmajor:
+        Ad, Bd, lda, ldb = to_dev(A, dtype), to_dev(B, dtype), K, K
+    else:
+        mp, np_ = -(-M // 8) * 8, -(-N // 8) * 8
+        At = np.zeros((K, mp), np.float32); At[:, :M] = A.T
+        Bt = np.zeros((K, np_), np.float32); Bt[:, :N] = B.T
+        Ad, Bd, lda, ldb = to_dev(At, dtype), to_dev(Bt, dtype), mp, np_
+    Cd = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    b.nc_op_matmul(DT[dtype], M, N, K, Ad.data_ptr(), lda, kmajor, Bd.data_ptr(), ldb, kmajor,
+                   Cd.data_ptr(), N, ws.data_ptr(), ws.numel(), stream())
+    torch.cuda.synchronize()
+    got = from_dev(Cd)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, want) < 2e-5
+
+
+def _qkv(Bn, T, H, hd, dtype, seed):
+    q = rand((Bn * T, H, hd), seed, dtype=dtype)
+    k = rand((Bn * T, hd), seed + 1, dtype=dtype)
+    v = rand((Bn * T, hd), seed + 2, dtype=dtype)
+    # unit-norm rows (as after QK-norm) scaled up so softmax is not uniform
+    q = q / np.sqrt(np.mean(q * q, -1, keepdims=True)) * 1.0
+    k = k / np.sqrt(np.mean(k * k, -1, keepdims=True)) * 1.0
+    if dtype == "bf16":
+        from nc_synth import bf16_round
+        q, k = bf16_round(q.astype(np.float32)), bf16_round(k.astype(np.float32))
+    return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
+
+
+def _pack_qkv(q, k, v):
+    n, H, hd = q.shape
+    buf = np.zeros((n, (H + 2) * hd), np.float32)
+    buf[:, :H * hd] = q.reshape(n, -1)
+    buf[:, H * hd:(H + 1) * hd] = k
+    buf[:, (H + 1) * hd:] = v
+    return buf
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Bn,T,H,hd", [(2, 128, 3, 64), (1, 192, 2, 128), (2, 64, 5, 128)])
+def test_attention_forward_backward(dtype, Bn, T, H, hd):
+    torch = require_gpu()
+    b = _b()
+    q, k, v = _qkv(Bn, T, H, hd, dtype, 10)
+    do = rand((Bn * T, H, hd), 20, dtype=dtype)
+    ld = (H + 2) * hd
+    buf = to_dev(_pack_qkv(q, k, v), dtype)
+    es = 2 if dtype == "bf16" else 4
+    base = buf.data_ptr()
+    o = torch.empty((Bn * T, H * hd), dtype=buf.dtype, device="cuda")
+    lse = torch.empty(Bn * T * H, dtype=torch.float32, device="cuda")
+    b.nc_op_attention_fwd(DT[dtype], Bn, T, H, hd, base, base + H * hd * es,
+                          base + (H + 1) * hd * es, ld, ld, o.data_ptr(), lse.data_ptr(), stream())
+    torch.cuda.synchronize()
+    want_o = np.concatenate([oracle.causal_mqa_attention(
+        q[i * T:(i + 1) * T].astype(np.float64), k[i * T:(i + 1) * T].astype(np.float64),
+        v[i * T:(i + 1) * T].astype(np.float64)) for i in range(Bn)])
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert rel_l2(from_dev(o).reshape(want_o.shape), want_o) < tol
+    # log-sum-exp of the scaled causal scores
+    s = np.einsum("thd,sd->ths", q.astype(np.float64).reshape(Bn, T, H, hd)[0],
+                  k.astype(np.float64)[:T]) / np.sqrt(hd)
+    future = np.arange(T)[:, None, None] < np.arange(T)[None, None, :]
+    s = np.where(future, -np.inf, s)
+    m = s.max(-1, keepdims=True)
+    want_lse = (m[..., 0] + np.log(np.exp(s - m).sum(-1))).reshape(-1)
+    assert rel_l2(from_dev(lse)[:T * H], want_lse) < 1e-5
+
+    # backward, with the GPU's own o as the forward output it differentiates
+    od = o
+    dod = to_dev(do.reshape(Bn * T, H * hd), dtype)
+    delta = torch.empty(Bn * T * H, dtype=torch.float32, device="cuda")
+    dq = torch.empty((Bn * T, H, hd), dtype=torch.float32, device="cuda")
+    dk = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
+    dv = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
+    b.nc_op_attention_bwd(DT[dtype], Bn, T, H, hd, base, base + H * hd * es,
+                          base + (H + 1) * hd * es, ld, ld, od.data_ptr(), dod.data_ptr(),
+                          lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), stream())
+    torch.cuda.synchronize()
+    wq, wk, wv = [], [], []
+    for i in range(Bn):
+        sl = slice(i * T, (i + 1) * T)
+        a, bb, c = oracle.causal_mqa_attention_backward(
+            q[sl].astype(np.float64), k[sl].astype(np.float64), v[sl].astype(np.float64),
+            do[sl].astype(np.float64))
+        wq.append(a); wk.append(bb); wv.append(c)
+    tolb = 1e-2 if dtype == "bf16" else 1e-5
+    assert rel_l2(from_dev(dq), np.concatenate(wq)) < tolb
+    assert rel_l2(from_dev(dk), np.concatenate(wk)) < tolb
+    assert rel_l2(from_dev(dv), np.concatenate(wv)) < tolb
+
+
+@pytest.mark.parametrize("dtype,V,ldz", [("bf16", 50257, 50432), ("bf16", 65536, 65536),
+                                          ("f32", 512, 512), ("bf16", 700, 768)])
+def test_softcap_cross_entropy(dtype, V, ldz):
+    torch = require_gpu()
+    b = _b()
+    n = 37
+    z = np.zeros((n, ldz), np.float32)
+    z[:, :V] = rand((n, V), 3, scale=20.0, dtype=dtype)
+    y = np.random.default_rng(4).integers(0, V, n).astype(np.int32)
+    y[0], y[1] = 0, V - 1
+    rs = np.random.default_rng(5).uniform(0.5, 2.0, n).astype(np.float32)
+    zd = to_dev(z, dtype)
+    yd = torch.from_numpy(y).cuda()
+    rsd = torch.from_numpy(rs).cuda()
+    tl = torch.empty(n, dtype=torch.float32, device="cuda")
+    b.nc_op_softcap_ce(DT[dtype], n, V, ldz, zd.data_ptr(), yd.data_ptr(), 15.0, rsd.data_ptr(),
+                       1.0 / n, tl.data_ptr(), True, stream())
+    torch.cuda.synchronize()
+    loss, dz = oracle.softcap_cross_entropy(z[:, :V].astype(np.float64), y, 15.0)
+    assert rel_l2(from_dev(tl), loss) < 1e-5
+    want = dz * (rs[:, None] / n)
+    got = from_dev(zd)
+    assert rel_l2(got[:, :V], want) < (1e-2 if dtype == "bf16" else 1e-5)
+    assert np.all(got[:, V:] == 0.0)
+
+
+@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_rope_qknorm(dtype, hd):
+    torch = require_gpu()
+    b = _b()
+    Bn, T, H = 2, 128, 3
+    x = rand((Bn * T, (H + 2) * hd), 6, dtype=dtype)
+    xd = to_dev(x, dtype)
+    rqk = torch.empty((Bn * T, H + 1), dtype=torch.float32, device="cuda")
+    tables = torch.empty(T * hd, dtype=torch.float32, device="cuda")
+    b.nc_op_rope_qknorm_fwd(DT[dtype], Bn, T, H, hd, xd.data_ptr(), 10000.0, 1e-6,
+                            rqk.data_ptr(), tables.data_ptr(), stream())
+    torch.cuda.synchronize()
+    cos, sin = oracle.rotary_tables(T, hd, 10000.0)
+    xs = x.astype(np.float64).reshape(Bn, T, H + 2, hd)
+    heads = xs[:, :, :H + 1]
+    rot = oracle.rotary(heads, cos[None, :, None, :], sin[None, :, None, :])
+    nrm, r = oracle.rms_norm(rot, 1e-6)
+    got = from_dev(xd).reshape(Bn, T, H + 2, hd)
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    assert rel_l2(got[:, :, :H + 1], nrm) < tol
+    np.testing.assert_array_equal(got[:, :, H + 1], xs[:, :, H + 1])
+    assert rel_l2(from_dev(rqk).reshape(Bn, T, H + 1), r[..., 0]) < 1e-5
