@@ -37,6 +37,11 @@ class nc_config(C.Structure):
         ("dtype", C.c_int32)]
 
 
+class nc_kernel_stat(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int32), ("total_ms", C.c_double),
+                ("flops", C.c_double), ("bytes", C.c_double)]
+
+
 class nc_tensor_info(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("offset", C.c_int64), ("rows", C.c_int32),
                 ("cols", C.c_int32)]
@@ -60,6 +65,9 @@ _sigs = {
     "nc_forward_loss": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "nc_forward_backward": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P, _P,
                                       C.c_size_t, _P]),
+    "nc_forward_backward_timed": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
+                                            C.c_size_t, _P, C.POINTER(nc_kernel_stat),
+                                            C.c_int32, C.POINTER(C.c_int32)]),
     "nc_validate_tokens": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P]),
     "nc_status_string": (C.c_char_p, [C.c_int]),
     "nc_last_hip_error": (C.c_int, []),
@@ -138,6 +146,18 @@ def nc_forward_backward(cfg, params, tokens, targets, loss, token_loss, grads, w
                         stream):
     _check("nc_forward_backward", _lib.nc_forward_backward(
         C.byref(cfg), params, tokens, targets, loss, token_loss, grads, ws, ws_bytes, stream))
+
+
+def nc_forward_backward_timed(cfg, params, tokens, targets, loss, grads, ws, ws_bytes, stream,
+                              cap: int = 64) -> list[dict]:
+    """Runs the step with per-launch events; returns one dict per kernel label."""
+    arr = (nc_kernel_stat * cap)()
+    n = C.c_int32()
+    _check("nc_forward_backward_timed", _lib.nc_forward_backward_timed(
+        C.byref(cfg), params, tokens, targets, loss, grads, ws, ws_bytes, stream, arr, cap,
+        C.byref(n)))
+    return [dict(name=a.name.decode(), launches=a.launches, ms=a.total_ms, flops=a.flops,
+                 bytes=a.bytes) for a in arr[:n.value]]
 
 
 def nc_validate_tokens(cfg, tokens, targets, n_bad, stream):

@@ -22,15 +22,14 @@ template <>
 hipError_t attn_fwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                             int64_t ldkv, bf16_t* o, float* lse, int B, int Tn, int H, int hd,
                             hipStream_t s) {
-    return attn_fwd_simt<bf16_t>(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
+    return attn_fwd_mfma(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
 }
 template <>
 hipError_t attn_bwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                             int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
                             float* delta, float* dq, float* dk, float* dv, int B, int Tn, int H,
                             int hd, hipStream_t s) {
-    return attn_bwd_simt<bf16_t>(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, Tn, H,
-                                 hd, s);
+    return attn_bwd_mfma(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, Tn, H, hd, s);
 }
 
 }  // namespace nc

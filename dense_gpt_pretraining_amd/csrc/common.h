@@ -122,4 +122,38 @@ __device__ __forceinline__ float tanh_f(float x) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ------------------------------------------------------------ matrix cores
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// D = A B + C for 32x32 fp32 blocks with K = 16 bf16 per instruction.  Lane l
+// supplies row (l & 31) of A and column (l & 31) of B, 8 consecutive k each
+// (k = 8 (l >> 5) .. +7); lane l receives column (l & 31) of D, rows
+// 8 (r / 4) + 4 (l >> 5) + (r % 4) for registers r = 0..15.
+__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
+                                           const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// transpose an 8 x 8 block of 16-bit values: in[r] holds row r (8 elements,
+// 2 per dword); out[c] receives column c
+__device__ __forceinline__ void transpose8x8(const uint4* in, uint4* out) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int d = c >> 1;
+        uint32_t w[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t x = reinterpret_cast<const uint32_t*>(&in[2 * p])[d];
+            const uint32_t y = reinterpret_cast<const uint32_t*>(&in[2 * p + 1])[d];
+            w[p] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
+        }
+        out[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 }  // namespace nc

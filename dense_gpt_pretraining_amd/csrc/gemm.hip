@@ -117,9 +117,6 @@ __global__ __launch_bounds__(256) void k_gemm_simt(int M, int N, int K, const T*
 }
 
 // ------------------------------------------------------------------ MFMA (bf16)
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kTM = 256, kTN = 256, kTK = 64;
 constexpr int kTileElems = kTM * kTK;                 // one operand tile (256 rows x 64 k)
 constexpr int kLdsBytes = 2 /*buffers*/ * 2 /*operands*/ * kTileElems * 2 /*bytes*/;
@@ -127,23 +124,6 @@ constexpr int kLdsBytes = 2 /*buffers*/ * 2 /*operands*/ * kTileElems * 2 /*byte
 // element offset of 16-byte chunk `ch` (0..7) of row `row` in a swizzled tile
 __device__ __forceinline__ int swz(int row, int ch) {
     return row * kTK + ((ch ^ ((row ^ (row >> 3)) & 7)) << 3);
-}
-
-// transpose an 8 x 8 block of 16-bit values: in[r] holds row r (8 elements,
-// 2 per dword); out[c] receives column c
-__device__ __forceinline__ void transpose8x8(const uint4* in, uint4* out) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int d = c >> 1;
-        uint32_t w[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t x = reinterpret_cast<const uint32_t*>(&in[2 * p])[d];
-            const uint32_t y = reinterpret_cast<const uint32_t*>(&in[2 * p + 1])[d];
-            w[p] = (c & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-        }
-        out[c] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
 }
 
 // Global -> registers for one 256-row x 64-k operand tile.

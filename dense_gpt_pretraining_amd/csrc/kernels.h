@@ -50,6 +50,14 @@ hipError_t attn_bwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_
 template <typename T>
 hipError_t attn_delta(const T* o, const T* dout, int64_t rows, int hd, float* delta,
                       hipStream_t s);
+// Matrix-core kernels (bf16, T a multiple of 64, hd 64 or 128).
+hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
+                         int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,
+                         hipStream_t s);
+hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
+                         int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
+                         float* delta, float* dq, float* dk, float* dv, int B, int T, int H,
+                         int hd, hipStream_t s);
 // Causal multi-query attention of B sequences of length T with H query heads
 // of width hd and one K/V head.  q: [B*T, H, hd] with token stride ldq;
 // k, v: [B*T, hd] with token stride ldkv; o: [B*T, H*hd]; lse: [B*T*H] fp32.

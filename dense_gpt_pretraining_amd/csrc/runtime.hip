@@ -172,6 +172,44 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
         }                                              \
     } while (0)
 
+// Per-launch HIP events for the timed step variant.
+struct Prof {
+    struct Rec {
+        const char* label;
+        double flops, bytes;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    hipStream_t s = nullptr;
+    hipError_t mark(hipEvent_t* ev) {
+        hipError_t e = hipEventCreate(ev);
+        if (e != hipSuccess) return e;
+        return hipEventRecord(*ev, s);
+    }
+    hipError_t done(const char* label, double flops, double bytes, hipEvent_t a) {
+        hipEvent_t b = nullptr;
+        hipError_t e = mark(&b);
+        recs.push_back({label, flops, bytes, a, b});
+        return e;
+    }
+    ~Prof() {
+        for (auto& r : recs) {
+            if (r.a) (void)hipEventDestroy(r.a);
+            if (r.b) (void)hipEventDestroy(r.b);
+        }
+    }
+};
+
+// run one launcher; with a profiler, bracket it with events and record its
+// algorithmic flops and HBM bytes under `label`
+#define NC_RUN(label, flops, bytes, expr)                                    \
+    do {                                                                     \
+        hipEvent_t a_ = nullptr;                                             \
+        if (prof) NC_TRY(prof->mark(&a_));                                   \
+        NC_TRY(expr);                                                        \
+        if (prof) NC_TRY(prof->done(label, (double)(flops), (double)(bytes), a_)); \
+    } while (0)
+
 template <typename T>
 struct Step {
     const nc_config& c;
@@ -179,11 +217,14 @@ struct Step {
     char* ws;
     hipStream_t s;
     const T* params;
+    Prof* prof;
     std::vector<TensorDesc> lay;
     int64_t N, D, H, hd, F, V, Vp, Wq;
 
-    Step(const nc_config& cfg, const Plan& plan, void* w, hipStream_t st, const void* prm)
-        : c(cfg), p(plan), ws(static_cast<char*>(w)), s(st), params(static_cast<const T*>(prm)) {
+    Step(const nc_config& cfg, const Plan& plan, void* w, hipStream_t st, const void* prm,
+         Prof* pr)
+        : c(cfg), p(plan), ws(static_cast<char*>(w)), s(st), params(static_cast<const T*>(prm)),
+          prof(pr) {
         lay = layout(c, nullptr);
         N = (int64_t)c.batch * c.seq_len;
         D = c.d_model; H = c.n_head; hd = c.head_dim; F = c.d_mlp; V = c.vocab;
@@ -195,21 +236,21 @@ struct Step {
         return reinterpret_cast<U*>(ws + base + (size_t)i * align256(per_bytes));
     }
     const T* W(int idx) const { return params + lay[idx].offset; }
-    // tensor indices in the layout
     int i_wte() const { return 0; }
     int i_layer(int l, int k) const { return 1 + 6 * l + k; }  // k: 0 wq,1 wk,2 wv,3 wo,4 wfc,5 wproj
     int i_wlm() const { return 1 + 6 * c.n_layer; }
 
-    size_t es() const { return sizeof(T); }
-    T* X(int i) { return slot<T>(p.x, i, N * D * es()); }
+    double es() const { return (double)sizeof(T); }
+    size_t ess() const { return sizeof(T); }
+    T* X(int i) { return slot<T>(p.x, i, N * D * ess()); }
     float* R1(int l) { return slot<float>(p.r1, l, N * 4); }
-    T* QKV(int l) { return slot<T>(p.qkv, l, N * Wq * es()); }
+    T* QKV(int l) { return slot<T>(p.qkv, l, N * Wq * ess()); }
     float* RQK(int l) { return slot<float>(p.rqk, l, N * (H + 1) * 4); }
-    T* O(int l) { return slot<T>(p.o, l, N * H * hd * es()); }
+    T* O(int l) { return slot<T>(p.o, l, N * H * hd * ess()); }
     float* LSE(int l) { return slot<float>(p.lse, l, N * H * 4); }
-    T* XM(int l) { return slot<T>(p.xm, l, N * D * es()); }
+    T* XM(int l) { return slot<T>(p.xm, l, N * D * ess()); }
     float* R2(int l) { return slot<float>(p.r2, l, N * 4); }
-    T* G(int l) { return slot<T>(p.g, l, N * F * es()); }
+    T* G(int l) { return slot<T>(p.g, l, N * F * ess()); }
 
     nc::Epilogue epi(int mode, const float* rs = nullptr, const void* aux = nullptr) {
         nc::Epilogue e;
@@ -218,13 +259,25 @@ struct Step {
         e.aux = aux;
         return e;
     }
+    // algorithmic work of a GEMM C[M,N] = A[M,K] B[N,K]^T: both operands read
+    // once, the output written once (out_es bytes per element), plus extra
+    // bytes the epilogue reads
+    double gf(int64_t m, int64_t n, int64_t k) const { return 2.0 * m * n * k; }
+    double gb(int64_t m, int64_t n, int64_t k, double out_es, double extra = 0) const {
+        return (double)(m * k + n * k) * es() + (double)m * n * out_es + extra;
+    }
+    // causal score pairs of one head over the batch: B * T(T+1)/2
+    double pairs() const { return (double)c.batch * c.seq_len * (c.seq_len + 1) / 2.0; }
 
     int forward(const int32_t* tok, const int32_t* tgt, float* loss, float* tok_loss, bool bwd) {
         const float eps = c.rms_eps;
         float* cos_t = at<float>(p.cos_t);
         float* sin_t = at<float>(p.sin_t);
-        NC_TRY(nc::rope_tables(c.seq_len, (int)hd, c.rope_base, cos_t, sin_t, s));
-        NC_TRY(nc::embed_fwd<T>(W(i_wte()), tok, (int)N, (int)D, eps, X(0), at<float>(p.r0), s));
+        const double rowb = (double)N * D * es();
+        NC_RUN("rope_tables", 0, c.seq_len * hd * 4.0,
+               nc::rope_tables(c.seq_len, (int)hd, c.rope_base, cos_t, sin_t, s));
+        NC_RUN("embed_fwd", 0, 2 * rowb + N * 8.0,
+               nc::embed_fwd<T>(W(i_wte()), tok, (int)N, (int)D, eps, X(0), at<float>(p.r0), s));
         const int L = c.n_layer;
         for (int l = 0; l < L; ++l) {
             const int sl = bwd ? l : 0;
@@ -232,33 +285,45 @@ struct Step {
             T* xn = X(bwd ? l + 1 : ((l + 1) & 1));
             float* r1 = R1(sl);
             T* qkv = QKV(sl);
-            NC_TRY(nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
+            NC_RUN("rms_stats", 0, rowb + N * 4.0,
+                   nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
+            NC_RUN("gemm_nt_rowscale", gf(N, Wq, D), gb(N, Wq, D, es(), N * 4.0),
+                   nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
                                Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
-            NC_TRY(nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t, sin_t,
+            NC_RUN("rope_qknorm_fwd", 0, 2.0 * N * (H + 1) * hd * es() + N * (H + 1) * 4.0,
+                   nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t, sin_t,
                                           eps, RQK(sl), s));
-            NC_TRY(nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
+            NC_RUN("attn_fwd", 4.0 * hd * H * pairs(),
+                   2.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 4.0,
+                   nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
                                    c.batch, c.seq_len, (int)H, (int)hd, s));
             T* xm = XM(sl);
-            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true, W(i_layer(l, 3)),
-                               H * hd, true, xm, D, epi(nc::EPI_RESID, nullptr, x), nullptr, 0, s));
+            NC_RUN("gemm_nt_resid", gf(N, D, H * hd), gb(N, D, H * hd, es(), rowb),
+                   nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true,
+                               W(i_layer(l, 3)), H * hd, true, xm, D,
+                               epi(nc::EPI_RESID, nullptr, x), nullptr, 0, s));
             float* r2 = R2(sl);
-            NC_TRY(nc::rms_stats<T>(xm, (int)N, (int)D, eps, r2, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)F, (int)D, xm, D, true, W(i_layer(l, 4)), D, true,
+            NC_RUN("rms_stats", 0, rowb + N * 4.0,
+                   nc::rms_stats<T>(xm, (int)N, (int)D, eps, r2, s));
+            NC_RUN("gemm_nt_relu2", gf(N, F, D), gb(N, F, D, es(), N * 4.0),
+                   nc::gemm<T>((int)N, (int)F, (int)D, xm, D, true, W(i_layer(l, 4)), D, true,
                                G(sl), F, epi(nc::EPI_ROWSCALE_RELU2, r2), nullptr, 0, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)F, G(sl), F, true, W(i_layer(l, 5)), F, true,
+            NC_RUN("gemm_nt_resid", gf(N, D, F), gb(N, D, F, es(), rowb),
+                   nc::gemm<T>((int)N, (int)D, (int)F, G(sl), F, true, W(i_layer(l, 5)), F, true,
                                xn, D, epi(nc::EPI_RESID, nullptr, xm), nullptr, 0, s));
         }
         T* hL = X(bwd ? L : (L & 1));
         float* rf = at<float>(p.rf);
-        NC_TRY(nc::rms_stats<T>(hL, (int)N, (int)D, eps, rf, s));
+        NC_RUN("rms_stats", 0, rowb + N * 4.0, nc::rms_stats<T>(hL, (int)N, (int)D, eps, rf, s));
         T* z = at<T>(p.z);
-        NC_TRY(nc::gemm<T>((int)N, (int)V, (int)D, hL, D, true, W(i_wlm()), D, true, z, Vp,
+        NC_RUN("gemm_nt_rowscale", gf(N, V, D), gb(N, V, D, es(), N * 4.0),
+               nc::gemm<T>((int)N, (int)V, (int)D, hL, D, true, W(i_wlm()), D, true, z, Vp,
                            epi(nc::EPI_ROWSCALE, rf), nullptr, 0, s));
         float* tl = tok_loss ? tok_loss : at<float>(p.tok_loss);
-        NC_TRY(nc::softcap_ce<T>(z, Vp, (int)V, (int)N, tgt, c.softcap, rf, 1.f / (float)N, tl,
+        NC_RUN("softcap_ce", 0, (bwd ? 2.0 : 1.0) * N * Vp * es() + N * 12.0,
+               nc::softcap_ce<T>(z, Vp, (int)V, (int)N, tgt, c.softcap, rf, 1.f / (float)N, tl,
                                  bwd, s));
-        NC_TRY(nc::mean_reduce(tl, (int)N, loss, s));
+        NC_RUN("mean_reduce", 0, N * 4.0 + 4, nc::mean_reduce(tl, (int)N, loss, s));
         return NC_OK;
     }
 
@@ -272,16 +337,23 @@ struct Step {
         float* dn = at<float>(p.dn);
         T* z = at<T>(p.z);  // now holds r_f/N * dloss/dz
         auto G_of = [&](int idx) { return grads + lay[idx].offset; };
+        // norm backward with residual: reads dn, x, dres; writes dres, dres_t
+        const double nbb = (double)N * D * (4 + es() + 4 + 4 + es()) + N * 4.0;
+        auto tb = [&](int64_t r, int64_t k) { return 2.0 * r * k * es(); };
 
         // head: df' = dz' W_lm, dW_lm = dz'^T h_L
         T* hL = X(L);
-        NC_TRY(nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
-        NC_TRY(nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
+        NC_RUN("transpose_w", 0, tb(V, D),
+               nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
+        NC_RUN("gemm_nt_f32", gf(N, D, V), gb(N, D, V, 4.0),
+               nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
                            epi(nc::EPI_STORE_F32), nullptr, 0, s));
-        NC_TRY(nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
+        NC_RUN("gemm_tn_f32", gf(V, D, N), gb(V, D, N, 4.0),
+               nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
                            epi(nc::EPI_STORE_F32), sk, skb, s));
-        NC_TRY(nc::zero_elems<float>(dres, N * D, s));
-        NC_TRY(nc::norm_bwd_resid<T>(dn, hL, at<float>(p.rf), (int)N, (int)D, dres, dres_t, s));
+        NC_RUN("zero", 0, N * D * 4.0, nc::zero_elems<float>(dres, N * D, s));
+        NC_RUN("norm_bwd_resid", 0, nbb,
+               nc::norm_bwd_resid<T>(dn, hL, at<float>(p.rf), (int)N, (int)D, dres, dres_t, s));
 
         T* dgu = at<T>(p.dgu);
         T* dout = at<T>(p.dout);
@@ -295,40 +367,64 @@ struct Step {
             T* x = X(l);
             T* xm = XM(l);
             // MLP: x_{l+1} = xm + relu(r2 xm W_fc^T)^2 W_proj^T
-            NC_TRY(nc::transpose<T>(W(i_layer(l, 5)), (int)D, (int)F, F, wt, D, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)F, (int)D, dres_t, D, true, wt, D, true, dgu, F,
+            NC_RUN("transpose_w", 0, tb(D, F),
+                   nc::transpose<T>(W(i_layer(l, 5)), (int)D, (int)F, F, wt, D, s));
+            NC_RUN("gemm_nt_relu2_bwd", gf(N, F, D), gb(N, F, D, es(), N * F * es() + N * 4.0),
+                   nc::gemm<T>((int)N, (int)F, (int)D, dres_t, D, true, wt, D, true, dgu, F,
                                epi(nc::EPI_RELU2_BWD, R2(l), G(l)), nullptr, 0, s));
-            NC_TRY(nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(l), F, false,
+            NC_RUN("gemm_tn_f32", gf(D, F, N), gb(D, F, N, 4.0),
+                   nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(l), F, false,
                                G_of(i_layer(l, 5)), F, epi(nc::EPI_STORE_F32), sk, skb, s));
-            NC_TRY(nc::transpose<T>(W(i_layer(l, 4)), (int)F, (int)D, D, wt, F, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)F, dgu, F, true, wt, F, true, dn, D,
+            NC_RUN("transpose_w", 0, tb(F, D),
+                   nc::transpose<T>(W(i_layer(l, 4)), (int)F, (int)D, D, wt, F, s));
+            NC_RUN("gemm_nt_f32", gf(N, D, F), gb(N, D, F, 4.0),
+                   nc::gemm<T>((int)N, (int)D, (int)F, dgu, F, true, wt, F, true, dn, D,
                                epi(nc::EPI_STORE_F32), nullptr, 0, s));
-            NC_TRY(nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
+            NC_RUN("gemm_tn_f32", gf(F, D, N), gb(F, D, N, 4.0),
+                   nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
                                G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
-            NC_TRY(nc::norm_bwd_resid<T>(dn, xm, R2(l), (int)N, (int)D, dres, dres_t, s));
+            NC_RUN("norm_bwd_resid", 0, nbb,
+                   nc::norm_bwd_resid<T>(dn, xm, R2(l), (int)N, (int)D, dres, dres_t, s));
             // attention: xm = x + o W_o^T
-            NC_TRY(nc::transpose<T>(W(i_layer(l, 3)), (int)D, (int)(H * hd), H * hd, wt, D, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)(H * hd), (int)D, dres_t, D, true, wt, D, true, dout,
+            NC_RUN("transpose_w", 0, tb(D, H * hd),
+                   nc::transpose<T>(W(i_layer(l, 3)), (int)D, (int)(H * hd), H * hd, wt, D, s));
+            NC_RUN("gemm_nt_store", gf(N, H * hd, D), gb(N, H * hd, D, es()),
+                   nc::gemm<T>((int)N, (int)(H * hd), (int)D, dres_t, D, true, wt, D, true, dout,
                                H * hd, epi(nc::EPI_STORE_T), nullptr, 0, s));
-            NC_TRY(nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(l), H * hd, false,
-                               G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb, s));
+            NC_RUN("gemm_tn_f32", gf(D, H * hd, N), gb(D, H * hd, N, 4.0),
+                   nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(l), H * hd,
+                               false, G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb,
+                               s));
             T* qkv = QKV(l);
-            NC_TRY(nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
+            NC_RUN("attn_bwd", 8.0 * hd * H * pairs(),
+                   4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
+                       4.0 * N * (H + 2) * hd,
+                   nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
                                    LSE(l), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
                                    (int)H, (int)hd, s));
-            NC_TRY(nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
+            NC_RUN("rope_qknorm_bwd", 0,
+                   N * (H + 1) * hd * es() + 4.0 * N * (H + 2) * hd + N * (H + 2) * hd * es() +
+                       N * (H + 2) * 4.0,
+                   nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
                                           (int)H, (int)hd, cos_t, sin_t, dqkv, s));
-            NC_TRY(nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
-            NC_TRY(nc::gemm<T>((int)N, (int)D, (int)Wq, dqkv, Wq, true, wt, Wq, true, dn, D,
+            NC_RUN("transpose_w", 0, tb(Wq, D),
+                   nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
+            NC_RUN("gemm_nt_f32", gf(N, D, Wq), gb(N, D, Wq, 4.0),
+                   nc::gemm<T>((int)N, (int)D, (int)Wq, dqkv, Wq, true, wt, Wq, true, dn, D,
                                epi(nc::EPI_STORE_F32), nullptr, 0, s));
-            NC_TRY(nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
+            NC_RUN("gemm_tn_f32", gf(Wq, D, N), gb(Wq, D, N, 4.0),
+                   nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
                                G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
-            NC_TRY(nc::norm_bwd_resid<T>(dn, x, R1(l), (int)N, (int)D, dres, dres_t, s));
+            NC_RUN("norm_bwd_resid", 0, nbb,
+                   nc::norm_bwd_resid<T>(dn, x, R1(l), (int)N, (int)D, dres, dres_t, s));
         }
         // embedding: h0 = r0 e, e = W_te[tok]
         float* de = dn;
-        NC_TRY(nc::embed_bwd_rows<T>(dres, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de, s));
-        NC_TRY(nc::embed_grad(de, tok, (int)N, (int)D, (int)V, G_of(i_wte()), ws + p.embed,
+        NC_RUN("embed_bwd_rows", 0, N * D * (4.0 + es() + 4.0),
+               nc::embed_bwd_rows<T>(dres, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de,
+                                     s));
+        NC_RUN("embed_grad", 0, N * D * 4.0 + (double)V * D * 4.0,
+               nc::embed_grad(de, tok, (int)N, (int)D, (int)V, G_of(i_wte()), ws + p.embed,
                               p.embed_bytes, s));
         return NC_OK;
     }
@@ -337,11 +433,11 @@ struct Step {
 template <typename T>
 int run_step(const nc_config& c, const void* params, const int32_t* tok, const int32_t* tgt,
              float* loss, float* tok_loss, float* grads, void* ws, size_t ws_bytes,
-             hipStream_t s) {
+             hipStream_t s, Prof* prof = nullptr) {
     const bool bwd = grads != nullptr;
     Plan p = make_plan(c, bwd);
     if (ws_bytes < p.bytes) return NC_ERR_WORKSPACE;
-    Step<T> st(c, p, ws, s, params);
+    Step<T> st(c, p, ws, s, params, prof);
     int rc = st.forward(tok, tgt, loss, tok_loss, bwd);
     if (rc != NC_OK || !bwd) return rc;
     return st.backward(tok, grads);
@@ -452,6 +548,47 @@ int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t*
                                     ws_bytes, s);
     return run_step<float>(*cfg, params, tokens, targets, loss, token_loss, grads, ws, ws_bytes,
                            s);
+}
+
+int nc_forward_backward_timed(const nc_config* cfg, const void* params, const int32_t* tokens,
+                              const int32_t* targets, float* loss, float* grads, void* ws,
+                              size_t ws_bytes, void* stream, nc_kernel_stat* stats, int32_t cap,
+                              int32_t* n_out) {
+    int rc = check_common(cfg, params, tokens, targets, loss, nullptr, ws);
+    if (rc != NC_OK) return rc;
+    if (!grads || !n_out || (cap > 0 && !stats)) return NC_ERR_NULL;
+    if (!aligned(grads, 256)) return NC_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Prof prof;
+    prof.s = s;
+    if (cfg->dtype == NC_BF16)
+        rc = run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, nullptr, grads, ws,
+                                  ws_bytes, s, &prof);
+    else
+        rc = run_step<float>(*cfg, params, tokens, targets, loss, nullptr, grads, ws, ws_bytes, s,
+                             &prof);
+    if (rc != NC_OK) return rc;
+    NC_TRY(hipStreamSynchronize(s));
+    std::vector<nc_kernel_stat> agg;
+    for (auto& r : prof.recs) {
+        float ms = 0.f;
+        NC_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+        size_t k = 0;
+        while (k < agg.size() && std::strcmp(agg[k].name, r.label) != 0) ++k;
+        if (k == agg.size()) {
+            nc_kernel_stat z;
+            std::memset(&z, 0, sizeof(z));
+            std::strncpy(z.name, r.label, sizeof(z.name) - 1);
+            agg.push_back(z);
+        }
+        agg[k].launches += 1;
+        agg[k].total_ms += ms;
+        agg[k].flops += r.flops;
+        agg[k].bytes += r.bytes;
+    }
+    *n_out = (int32_t)agg.size();
+    for (size_t k = 0; k < agg.size() && (int32_t)k < cap; ++k) stats[k] = agg[k];
+    return cap < (int32_t)agg.size() ? NC_ERR_CAPACITY : NC_OK;
 }
 
 int nc_validate_tokens(const nc_config* cfg, const int32_t* tokens, const int32_t* targets,

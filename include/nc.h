@@ -12,9 +12,11 @@
  * n(u) = u / sqrt(mean(u^2) + eps) everywhere, with no learnable gain.
  *
  * Conventions shared by every function:
- *   - Every pointer except `cfg`, `n_elems`, `bytes`, `out`/`n_out` (host
- *     structs and counters) is a DEVICE pointer.  Device buffers must be
- *     256-byte aligned (torch allocations are); otherwise NC_ERR_ALIGN.
+ *   - Every pointer except `cfg`, `n_elems`, `bytes`, `out`/`stats`/`n_out`
+ *     (host structs and counters) is a DEVICE pointer.  params, grads and ws
+ *     must be 256-byte aligned, tokens, targets and token_loss 16-byte
+ *     aligned, loss and n_bad 4-byte aligned (torch allocations are);
+ *     otherwise NC_ERR_ALIGN.
  *   - The caller owns every buffer.  The library allocates no device memory
  *     and keeps no mutable global state, so calls on different streams with
  *     different workspaces may run concurrently.
@@ -147,6 +149,32 @@ int nc_forward_backward(const nc_config* cfg, const void* params,
                         const int32_t* tokens, const int32_t* targets,
                         float* loss, float* token_loss, float* grads, void* ws,
                         size_t ws_bytes, void* stream);
+
+/* per-kernel account of one step (nc_forward_backward_timed) */
+typedef struct nc_kernel_stat {
+    char name[48];      /* kernel label, e.g. "gemm_nt_relu2" */
+    int32_t launches;   /* launches of this kernel in the step */
+    double total_ms;    /* summed durations, HIP events on `stream` around each launch */
+    double flops;       /* algorithmic floating-point operations, summed over launches */
+    double bytes;       /* algorithmic HBM bytes (each input read once, each output
+                           written once), summed over launches */
+} nc_kernel_stat;
+
+/*
+ * nc_forward_backward with a HIP event recorded on `stream` before and after
+ * every kernel launch.  Same outputs and arguments as nc_forward_backward,
+ * plus `stats` (host array of `cap` entries) that receives one entry per
+ * distinct kernel label, in first-launch order; *n_out is the number of
+ * labels (NC_ERR_CAPACITY if cap is smaller, stats then holds the first cap).
+ * Unlike the other calls this one synchronises `stream` before returning.
+ * The events serialise nothing that stream order does not already serialise.
+ */
+int nc_forward_backward_timed(const nc_config* cfg, const void* params,
+                              const int32_t* tokens, const int32_t* targets,
+                              float* loss, float* grads, void* ws,
+                              size_t ws_bytes, void* stream,
+                              nc_kernel_stat* stats, int32_t cap,
+                              int32_t* n_out);
 
 /*
  * Count ids outside [0, vocab) in tokens and targets (B*T each) into *n_bad
