@@ -5,18 +5,25 @@
 // gradient dW = dY^T X; all three are this one contraction with the operands
 // read either along k ("k-major") or along m/n ("mn-major").
 //
-// bf16: CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16).  A 256-thread
-// workgroup owns a 256 (m) x 256 (n) output tile; each of its 4 waves owns a
-// 128 x 128 quadrant held as 4 x 4 accumulator blocks of 32 x 32 fp32.  The
-// k loop stages 256 x 64 tiles of both operands in LDS, double-buffered, with
-// an XOR swizzle of the 16-byte chunks of each row so that neither the
-// fragment reads (8 consecutive rows, same chunk) nor the transposing writes
-// (rows 8 apart, same chunk) collide in a bank group.  mn-major operands are
-// loaded as 8 x 8 element blocks and transposed in registers before the LDS
-// write, so the fragment reads are the same 16-byte reads for every layout.
+// bf16: CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16).  A 512-thread
+// workgroup (8 waves, two per SIMD) owns a 256 (m) x 256 (n) output tile;
+// wave w owns 64 m rows x 128 n rows, held as 2 x 4 accumulator blocks of
+// 32 x 32 fp32.  The k loop stages 256 x 64 tiles of both operands in two
+// LDS buffers with an XOR swizzle of the 16-byte chunks of each row, so
+// fragment reads of 8 or 16 consecutive rows at one logical chunk hit
+// distinct banks (the bank-conflict counter reads zero).
+//   k-major operands go straight from global memory into LDS
+//   (global_load_lds_dwordx4, no staging registers); the loads of tile k+1
+//   are in flight while tile k is multiplied, and the fragments of k step
+//   s+1 are read while the matrix instructions of step s issue.
+//   mn-major operands (the weight-gradient layout) are loaded as 8 x 8 blocks
+//   into registers and transposed before the LDS write, so fragment reads are
+//   the same 16-byte reads for every layout.
 // The MFMA "A" side takes the n rows and the "B" side the m rows, which puts
 // 4 consecutive n of one row m in each lane's accumulator registers: the
 // epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
+// Tiles are visited XCD by XCD (each of the 8 dies gets a contiguous range)
+// and in groups of 8 m-tiles, so the operand rows they share stay in L2.
 //
 // fp32: a plain LDS-tiled SIMT kernel (64 x 64 tiles, 4 x 4 per thread).
 #include "kernels.h"
@@ -118,67 +125,97 @@ __global__ __launch_bounds__(256) void k_gemm_simt(int M, int N, int K, const T*
 
 // ------------------------------------------------------------------ MFMA (bf16)
 constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kThreads = 512;                         // 8 waves, 2 per SIMD
 constexpr int kTileElems = kTM * kTK;                 // one operand tile (256 rows x 64 k)
-constexpr int kLdsBytes = 2 /*buffers*/ * 2 /*operands*/ * kTileElems * 2 /*bytes*/;
 
 // element offset of 16-byte chunk `ch` (0..7) of row `row` in a swizzled tile
-__device__ __forceinline__ int swz(int row, int ch) {
-    return row * kTK + ((ch ^ ((row ^ (row >> 3)) & 7)) << 3);
+__device__ __forceinline__ int swz_f(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row, int ch) { return row * kTK + ((ch ^ swz_f(row)) << 3); }
+
+// Stage one 256-row x 64-k operand tile into LDS.
+//   k-major: straight from global memory into LDS (global_load_lds_dwordx4).
+//     Wave w's instruction i fills the 64 consecutive 16-byte LDS slots of
+//     rows 64 i + 8 w .. +7, so lane l holds row 64 i + 8 w + (l >> 3) at
+//     physical chunk l & 7, i.e. logical chunk (l & 7) ^ (l >> 3) ^ w under
+//     the swizzle -- the same for every i.  Each lane therefore keeps one
+//     32-bit offset per instruction from a uniform tile base that advances
+//     by 64 columns per k step.  Rows past `rows` are clamped to the last row
+//     (those outputs are never stored).  Requires k0 + 64 <= K.
+//   mn-major: 256 threads (half of the workgroup) each load an 8 (k) x 8 (row)
+//     block into registers; tile_store_mn transposes and writes it.
+struct KmajLoads {
+    uint32_t off[4];   // byte offsets of this lane's four chunks from the tile base
+};
+
+__device__ __forceinline__ KmajLoads kmaj_offsets(int64_t ld, int rows, int r0, int w, int lane) {
+    KmajLoads L;
+    const int lc = (lane & 7) ^ (lane >> 3) ^ w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = min(r0 + 64 * i + 8 * w + (lane >> 3), rows - 1) - r0;
+        L.off[i] = (uint32_t)(((int64_t)row * ld + lc * 8) * 2);
+    }
+    return L;
 }
 
-// Global -> registers for one 256-row x 64-k operand tile.
-//   k-major: thread t loads rows (t>>3) + 32 i, chunk t&7   (i = 0..7)
-//   mn-major: thread t loads k rows 8 (t>>5) + i at row chunk t&31
-template <bool KMAJ>
-__device__ __forceinline__ void tile_load(const bf16_t* __restrict__ P, int64_t ld, int rows,
-                                          int K, int r0, int k0, uint4* reg) {
-    const int t = threadIdx.x;
-    if (KMAJ) {
-        const int ch = t & 7;
-        const int k = k0 + ch * 8;
+// tile_base points at element (r0, k0) of the operand; T is the LDS tile
+__device__ __forceinline__ void kmaj_issue(const bf16_t* tile_base, const KmajLoads& L, bf16_t* T,
+                                           int w) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = r0 + (t >> 3) + 32 * i;
-            if (r < rows && k < K)
-                reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)r * ld + k);
-            else
-                reg[i] = make_uint4(0, 0, 0, 0);
-        }
-    } else {
-        const int r = r0 + (t & 31) * 8;
-        const int kb = k0 + (t >> 5) * 8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int k = kb + i;
-            if (r < rows && k < K)
-                reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)k * ld + r);
-            else
-                reg[i] = make_uint4(0, 0, 0, 0);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const char* g = reinterpret_cast<const char*>(tile_base) + L.off[i];
+        __builtin_amdgcn_global_load_lds(
+            (const void*)g, (__attribute__((address_space(3))) void*)(T + (i * 8 + w) * 512), 16,
+            0, 0);
     }
 }
 
 template <bool KMAJ>
-__device__ __forceinline__ void tile_store(bf16_t* __restrict__ S, const uint4* reg) {
-    const int t = threadIdx.x;
-    if (KMAJ) {
-        const int ch = t & 7;
+__device__ __forceinline__ void mn_load(const bf16_t* __restrict__ P, int64_t ld, int rows,
+                                        int K, int r0, int k0, uint4* reg, int half) {
+    const int tid = threadIdx.x;
+    if ((tid >> 8) != half) return;
+    const int t = tid & 255;
+    const int r = r0 + (t & 31) * 8;
+    const int kb = k0 + (t >> 5) * 8;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = (t >> 3) + 32 * i;
-            *reinterpret_cast<uint4*>(S + swz(r, ch)) = reg[i];
-        }
-    } else {
-        uint4 tr[8];
-        transpose8x8(reg, tr);
-        const int ch = t >> 5;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int r = (t & 31) * 8 + c;
-            *reinterpret_cast<uint4*>(S + swz(r, ch)) = tr[c];
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int k = kb + i;
+        if (r < rows && k < K)
+            reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)k * ld + r);
+        else
+            reg[i] = make_uint4(0, 0, 0, 0);
     }
 }
+
+__device__ __forceinline__ void tile_store_mn(bf16_t* T, const uint4* reg, int half) {
+    const int tid = threadIdx.x;
+    if ((tid >> 8) != half) return;
+    const int t = tid & 255;
+    uint4 tr[8];
+    transpose8x8(reg, tr);
+    const int ch = t >> 5;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int r = (t & 31) * 8 + c;
+        *reinterpret_cast<uint4*>(T + swz(r, ch)) = tr[c];
+    }
+}
+
+// wait until this thread's direct global->LDS loads have landed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// workgroup barrier without the memory fence __syncthreads() implies: the
+// fence would wait for every outstanding load, including the direct loads of
+// tiles still in flight.  LDS data the barrier publishes has landed through an
+// explicit vmcnt wait; the empty asm keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 
 __device__ __forceinline__ int xcd_remap(int pid, int total) {
     // consecutive workgroup ids land on different XCDs (round robin over 8);
@@ -228,14 +265,44 @@ __device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, 
     }
 }
 
+// 512 threads: wave w owns m rows wm*64 .. +63 (wm = w & 3) and n rows
+// wn*128 .. +127 (wn = w >> 2) of the 256 x 256 tile: 2 x 4 accumulator blocks.
+// A fragment row 32 i + (lane & 31) of a 32-aligned block has swizzle
+// f0 ^ 4 (i & 1) with f0 that of (lane & 31), so the chunk offsets of the 4
+// k steps for the two parities are precomputed per lane (foff) and every
+// fragment read is base + constant.
+__device__ __forceinline__ void mma_tile(const bf16_t* sA, const bf16_t* sB, f32x16_t (&acc)[4][2],
+                                         const int (&foff)[2][4], int wm, int wn, int lane) {
+    const int rowoff = (lane & 31) * kTK;
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ++ks) {
+        bf16x8_t fa[4], fb[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            fb[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
+    }
+}
+
 template <bool AK, bool BK, int MODE>
-__global__ __launch_bounds__(256, 1) void k_gemm_mfma(int M, int N, int K, int k_per_split,
-                                                      const bf16_t* __restrict__ A, int64_t lda,
-                                                      const bf16_t* __restrict__ B, int64_t ldb,
-                                                      void* C, int64_t ldc, EpiDev e,
-                                                      int64_t split_stride) {
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    bf16_t* lds = reinterpret_cast<bf16_t*>(lds_raw);
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, int k_per_split,
+                                                           const bf16_t* __restrict__ A,
+                                                           int64_t lda,
+                                                           const bf16_t* __restrict__ B,
+                                                           int64_t ldb, void* C, int64_t ldc,
+                                                           EpiDev e, int64_t split_stride) {
+    // two distinct buffers (A tile then B tile each), so the compiler can see
+    // that loads into one never alias reads of the other
+    __shared__ __align__(16) bf16_t lds0[2 * kTileElems];
+    __shared__ __align__(16) bf16_t lds1[2 * kTileElems];
 
     const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     const int total = tiles_m * tiles_n;
@@ -251,72 +318,113 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mfma(int M, int N, int K, int k
 
     const int kb = blockIdx.z * k_per_split;
     const int ke = min(K, kb + k_per_split);
-    if (e.mode == EPI_STORE_F32 && split_stride) C = static_cast<float*>(C) + blockIdx.z * split_stride;
+    if (MODE == EPI_STORE_F32 && split_stride)
+        C = static_cast<float*>(C) + blockIdx.z * split_stride;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    int foff[2][4];
+    {
+        const int fr = lane & 31, fch = lane >> 5;
+        const int f0 = (fr ^ (fr >> 3)) & 7;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) foff[p][ks] = ((2 * ks + fch) ^ f0 ^ (4 * p)) << 3;
+    }
+
+    KmajLoads la, lb;
+    if (AK) la = kmaj_offsets(lda, M, m0, wave, lane);
+    if (BK) lb = kmaj_offsets(ldb, N, n0, wave, lane);
     uint4 ra[8], rb[8];
     const int nk = (ke - kb + kTK - 1) / kTK;
+    auto issue = [&](int kt, bf16_t* buf) {
+        const int k0 = kb + kt * kTK;
+        if (AK) kmaj_issue(A + (int64_t)m0 * lda + k0, la, buf, wave);
+        else mn_load<false>(A, lda, M, ke, m0, k0, ra, 0);
+        if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, buf + kTileElems, wave);
+        else mn_load<false>(B, ldb, N, ke, n0, k0, rb, 1);
+    };
+    auto finish = [&](bf16_t* buf) {
+        if (!AK) tile_store_mn(buf, ra, 0);
+        if (!BK) tile_store_mn(buf + kTileElems, rb, 1);
+        if (AK || BK) wait_vmem();
+    };
     if (nk > 0) {
-        tile_load<AK>(A, lda, M, ke, m0, kb, ra);
-        tile_load<BK>(B, ldb, N, ke, n0, kb, rb);
-        tile_store<AK>(lds, ra);
-        tile_store<BK>(lds + kTileElems, rb);
+        issue(0, lds0);
+        finish(lds0);
     }
     __syncthreads();
-
-    const int frow = lane & 31, fch = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int k0 = kb + (kt + 1) * kTK;
-            tile_load<AK>(A, lda, M, ke, m0, k0, ra);
-            tile_load<BK>(B, ldb, N, ke, n0, k0, rb);
-        }
-        const bf16_t* sA = lds + cur * 2 * kTileElems;
-        const bf16_t* sB = sA + kTileElems;
-#pragma unroll
-        for (int ks = 0; ks < kTK / 16; ++ks) {
-            bf16x8_t fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rn = wn * 128 + i * 32 + frow;
-                const uint4 v = *reinterpret_cast<const uint4*>(sB + swz(rn, 2 * ks + fch));
-                fa[i] = __builtin_bit_cast(bf16x8_t, v);
-                const int rm = wm * 128 + i * 32 + frow;
-                const uint4 w = *reinterpret_cast<const uint4*>(sA + swz(rm, 2 * ks + fch));
-                fb[i] = __builtin_bit_cast(bf16x8_t, w);
-            }
+    if (AK && BK) {
+        // fragments of k step ks+1 (or of the next tile's first step) are
+        // read while the 8 matrix instructions of step ks issue
+        const int rowoff = (lane & 31) * kTK;
+        bf16x8_t fa[2][4], fb[2][2];
+        auto rd = [&](const bf16_t* buf, int ks, int set) {
+            const bf16_t* sA = buf;
+            const bf16_t* sB = buf + kTileElems;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+                fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]));
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 2; ++j)
+                fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]));
+        };
+        for (int kt = 0; kt < nk; ++kt) {
+            bf16_t* cur = (kt & 1) ? lds1 : lds0;
+            bf16_t* nxt = (kt & 1) ? lds0 : lds1;
+            if (kt > 0) {
+                // tile kt has landed (this wave's loads) and every wave is
+                // done reading tile kt-1, whose buffer is refilled next
+                wait_vmem();
+                barrier_nofence();
+            }
+            if (kt + 1 < nk) issue(kt + 1, nxt);
+            rd(cur, 0, 0);
+#pragma unroll
+            for (int ks = 0; ks < kTK / 16; ++ks) {
+                const int cs = ks & 1;
+                if (ks + 1 < kTK / 16) rd(cur, ks + 1, cs ^ 1);
+                // keep the next step's reads ahead of this step's products
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (more) {
-            bf16_t* nA = lds + (cur ^ 1) * 2 * kTileElems;
-            tile_store<AK>(nA, ra);
-            tile_store<BK>(nA + kTileElems, rb);
+    } else {
+        for (int kt = 0; kt < nk; ++kt) {
+            bf16_t* cur = (kt & 1) ? lds1 : lds0;
+            bf16_t* nxt = (kt & 1) ? lds0 : lds1;
+            const bool more = kt + 1 < nk;
+            if (more) issue(kt + 1, nxt);
+            mma_tile(cur, cur + kTileElems, acc, foff, wm, wn, lane);
+            if (more) finish(nxt);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
-    // epilogue: lane holds m = m0 + wm*128 + 32 j + (lane & 31) and, for
+    // epilogue: lane holds m = m0 + wm*64 + 32 j + (lane & 31) and, for
     // register group g, n = n0 + wn*128 + 32 i + 8 g + 4 (lane >> 5) + 0..3
     const bool full_n = n0 + kTN <= N;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 128 + 32 * j + (lane & 31);
+    for (int j = 0; j < 2; ++j) {
+        const int64_t m = m0 + wm * 64 + 32 * j + (lane & 31);
         if (m >= M) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -361,16 +469,12 @@ template <bool AK, bool BK, int MODE>
 hipError_t launch_mfma(int M, int N, int K, const bf16_t* A, int64_t lda, const bf16_t* B,
                        int64_t ldb, void* C, int64_t ldc, const EpiDev& e, int splits,
                        int64_t split_stride, hipStream_t s) {
-    auto kern = k_gemm_mfma<AK, BK, MODE>;
-    // allow more than 64 KiB of dynamic LDS (set once per process; idempotent)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (attr != hipSuccess) return attr;
     int k_per = (int)ceil_div(K, splits);
     k_per = (int)ceil_div(k_per, kTK) * kTK;
     const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
-    hipLaunchKernelGGL(kern, dim3(tiles, 1, splits), dim3(256), kLdsBytes, s, M, N, K, k_per, A,
-                       lda, B, ldb, C, ldc, e, split_stride);
+    auto kern = k_gemm_mfma<AK, BK, MODE>;
+    hipLaunchKernelGGL(kern, dim3(tiles, 1, splits), dim3(kThreads), 0, s, M, N, K, k_per, A, lda,
+                       B, ldb, C, ldc, e, split_stride);
     return hipGetLastError();
 }
 

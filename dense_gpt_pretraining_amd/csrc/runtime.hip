@@ -44,7 +44,8 @@ int validate(const nc_config* c) {
         return NC_ERR_CONFIG;
     if (c->head_dim != 64 && c->head_dim != 128) return NC_ERR_UNSUPPORTED;
     if (c->n_kv_head != 1) return NC_ERR_UNSUPPORTED;
-    if (c->d_model % 8 || c->d_mlp % 8) return NC_ERR_UNSUPPORTED;
+    // k-major GEMM operands are staged 64 columns at a time straight into LDS
+    if (c->d_model % 64 || c->d_mlp % 64) return NC_ERR_UNSUPPORTED;
     if (c->seq_len % 64) return NC_ERR_UNSUPPORTED;
     if (c->softcap > 60.f) return NC_ERR_UNSUPPORTED;
     if (c->vocab > (1 << 24)) return NC_ERR_UNSUPPORTED;

@@ -59,11 +59,11 @@ enum {
 /*
  * Model and batch description.
  *   n_layer    number of blocks (>= 1)
- *   d_model    width D of the residual stream (multiple of 8)
+ *   d_model    width D of the residual stream (multiple of 64)
  *   n_head     H, query heads; n_head * head_dim is the attention width
  *   head_dim   hd, 64 or 128
  *   n_kv_head  must be 1: multi-query attention (one K head, one V head)
- *   d_mlp      F, hidden width of the relu^2 MLP (multiple of 8)
+ *   d_mlp      F, hidden width of the relu^2 MLP (multiple of 64)
  *   vocab      V >= 2
  *   seq_len    T, a multiple of 64
  *   batch      B >= 1 sequences; tokens per step N = B*T

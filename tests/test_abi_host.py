@@ -68,7 +68,7 @@ def test_workspace_sizes_are_monotone():
 @pytest.mark.parametrize("field,value,code", [
     ("n_layer", 0, -2), ("vocab", 1, -2), ("batch", 0, -2), ("d_model", 4, -2),
     ("head_dim", 96, -7), ("n_kv_head", 2, -7), ("seq_len", 100, -7), ("dtype", 5, -3),
-    ("softcap", 0.0, -2), ("softcap", 100.0, -7), ("rms_eps", -1.0, -2), ("d_mlp", 12, -7),
+    ("softcap", 0.0, -2), ("softcap", 100.0, -7), ("rms_eps", -1.0, -2), ("d_mlp", 12, -7), ("d_model", 136, -7),
 ])
 def test_bad_configs_are_rejected(field, value, code):
     b = _b()

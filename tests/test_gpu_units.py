@@ -27,7 +27,7 @@ def _b():
 @pytest.mark.parametrize("M,N,K,kmajor", [
     (300, 520, 192, True),      # several 256 tiles, ragged m and n tails
     (256, 256, 64, True),       # exactly one tile
-    (1, 8, 8, True),            # degenerate
+    (1, 8, 64, True),           # degenerate m, n
     (264, 136, 1000, False),    # mn-major operands (weight-gradient layout), ragged k
     (512, 768, 4096, False),    # long k: split over the k loop
 ])
