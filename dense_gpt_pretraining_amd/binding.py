@@ -77,7 +77,8 @@ _sigs = {
     "nc_op_attention_fwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
                                                           _P]),
     "nc_op_attention_bwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
-                                                          _P, _P, _P, _P, _P, _P]),
+                                                          _P, _P, C.c_size_t, _P, _P, _P, _P]),
+    "nc_op_attention_bwd_scratch_bytes": (C.c_int, [C.c_int32] * 4 + [C.POINTER(C.c_size_t)]),
     "nc_op_softcap_ce": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int64, _P, _P, C.c_float,
                                    _P, C.c_float, _P, C.c_int32, _P]),
     "nc_op_rope_qknorm_fwd": (C.c_int, [C.c_int32] * 5 + [_P, C.c_float, C.c_float, _P, _P, _P]),
@@ -184,10 +185,18 @@ def nc_op_attention_fwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, lse, stream):
                                                            ldkv, o, lse, stream))
 
 
-def nc_op_attention_bwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk,
-                        dv, stream):
+def nc_op_attention_bwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, dout, lse, scratch,
+                        scratch_bytes, dq, dk, dv, stream):
     _check("nc_op_attention_bwd", _lib.nc_op_attention_bwd(
-        dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, stream))
+        dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, dout, lse, scratch, scratch_bytes, dq, dk, dv,
+        stream))
+
+
+def nc_op_attention_bwd_scratch_bytes(B, T, H, hd) -> int:
+    n = C.c_size_t()
+    _check("nc_op_attention_bwd_scratch_bytes",
+           _lib.nc_op_attention_bwd_scratch_bytes(B, T, H, hd, C.byref(n)))
+    return n.value
 
 
 def nc_op_softcap_ce(dtype, N, V, ldz, z, targets, softcap, rowscale, inv_n, tok_loss,

@@ -13,10 +13,11 @@ hipError_t attn_fwd<float>(const float* q, const float* k, const float* v, int64
 template <>
 hipError_t attn_bwd<float>(const float* q, const float* k, const float* v, int64_t ldq,
                            int64_t ldkv, const float* o, const float* dout, const float* lse,
-                           float* delta, float* dq, float* dk, float* dv, int B, int Tn, int H,
+                           float* scratch, float* dq, float* dk, float* dv, int B, int Tn, int H,
                            int hd, hipStream_t s) {
-    return attn_bwd_simt<float>(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, Tn, H, hd,
-                                s);
+    // the per-row kernels need only the row sums (first B*T*H floats)
+    return attn_bwd_simt<float>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, Tn, H,
+                                hd, s);
 }
 template <>
 hipError_t attn_fwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
@@ -27,9 +28,9 @@ hipError_t attn_fwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, i
 template <>
 hipError_t attn_bwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                             int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
-                            float* delta, float* dq, float* dk, float* dv, int B, int Tn, int H,
+                            float* scratch, float* dq, float* dk, float* dv, int B, int Tn, int H,
                             int hd, hipStream_t s) {
-    return attn_bwd_mfma(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, Tn, H, hd, s);
+    return attn_bwd_mfma(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, Tn, H, hd, s);
 }
 
 }  // namespace nc

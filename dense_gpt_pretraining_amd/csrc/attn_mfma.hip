@@ -378,12 +378,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
 constexpr int kKB = 128;   // keys per workgroup (4 waves x 32)
 constexpr int kQT = 32;    // query rows per tile
 
+// The query rows a key block can see are cut into chunks of `chunk_rows`
+// (a multiple of kQT); chunk c of key block kb of sequence b is one workgroup,
+// which writes its dK, dV sums to partial slot (b, first_slot(kb) + c).  The
+// number of chunks of key block kb is chunks_of(kb).
+__host__ __device__ __forceinline__ int kv_rows_begin(int kb, int H) {
+    return (kb * kKB * H) / kQT * kQT;
+}
+__host__ __device__ __forceinline__ int kv_chunks(int kb, int H, int rows_total, int chunk_rows) {
+    return (rows_total - kv_rows_begin(kb, H) + chunk_rows - 1) / chunk_rows;
+}
+
 template <int HD>
 __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv, int B,
-    int T, int H, float scale_log2, float scale) {
+    const float* __restrict__ delta, float* __restrict__ dk_part, float* __restrict__ dv_part,
+    int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq) {
     constexpr int KCH = HD / 8;
     constexpr int QTILE = kQT * HD;                  // elements of one row tile
     constexpr int BLK = (kQT / 8) * (HD / 8);        // 8x8 blocks of one row tile
@@ -393,9 +404,17 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
 
     const int rows_total = T * H;
     const int n_kb = (T + kKB - 1) / kKB;
-    const int kbi = (int)(blockIdx.x / B);            // key block 0 (heaviest) first
     const int b = (int)(blockIdx.x % B);
-    (void)n_kb;
+    int rest = (int)(blockIdx.x / B), kbi = 0, slot = 0;
+    for (; kbi < n_kb; ++kbi) {
+        const int nc = kv_chunks(kbi, H, rows_total, chunk_rows);
+        if (rest < nc) break;
+        rest -= nc;
+        slot += nc;
+    }
+    slot += rest;
+    const int r_begin = kv_rows_begin(kbi, H) + rest * chunk_rows;
+    const int r_end = min(r_begin + chunk_rows, rows_total);
     const int64_t seq0 = (int64_t)b * T;
     const int key0 = kbi * kKB;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
@@ -417,8 +436,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) { dka[db] = zero16(); dva[db] = zero16(); }
 
-    const int r_begin = (key0 * H) / kQT * kQT;
-    const int n_qt = (rows_total - r_begin + kQT - 1) / kQT;
+    const int n_qt = (r_end - r_begin + kQT - 1) / kQT;
 
     uint4 reg[8];
     float lreg = 0.f;
@@ -429,16 +447,20 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
             const int blk = tid % BLK;
             const bool is_do = tid >= BLK;
             const int rb8 = blk % (kQT / 8), db8 = blk / (kQT / 8);
+            // position and head of the block's first row; later rows step j
+            const int row0 = R0 + rb8 * 8;
+            int t = row0 / H, j = row0 - t * H;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int row = R0 + rb8 * 8 + i;
+                const int row = row0 + i;
                 if (row < rows_total) {
                     const bf16_t* src = is_do ? dout + (seq0 * H + row) * HD
-                                              : q + (seq0 + row / H) * ldq + (int64_t)(row % H) * HD;
+                                              : q + (seq0 + t) * ldq + (int64_t)j * HD;
                     reg[i] = *reinterpret_cast<const uint4*>(src + db8 * 8);
                 } else {
                     reg[i] = make_uint4(0, 0, 0, 0);
                 }
+                if (++j == H) { j = 0; ++t; }
             }
         } else if (tid < 2 * BLK + 2 * kQT) {
             const int x = tid - 2 * BLK;
@@ -487,8 +509,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
         const float* sL = reinterpret_cast<const float*>(base + 4 * QTILE);
         // rows of this tile reach keys up to their position; skip the tile if
         // even its last row precedes this wave's first key
-        const int t_last = min(R0 + kQT - 1, rows_total - 1) / H;
-        if (wvalid && t_last >= wkey0) {
+        // some row of the tile sees this wave's first key iff its last row
+        // r satisfies r >= wkey0 * H
+        if (wvalid && min(R0 + kQT - 1, rows_total - 1) >= wkey0 * H) {
             f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
@@ -499,13 +522,15 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
                     sD + rt_off<KCH>(li, 2 * kk + g)));
                 dp = mfma32(ad, vf[kk], dp);
             }
-            // lane holds key `key`; register rr holds row R0 + 8(rr/4) + 4g + rr%4
+            // lane holds key `key`; register rr holds row R0 + 8(rr/4) + 4g + rr%4.
+            // Row r sits at position r / H, and key <= r / H exactly when r >= key * H.
             float p[16], ds[16];
+            const int first_vis = key * H;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int ro = 8 * (rr >> 2) + 4 * g + (rr & 3);
                 const int row = R0 + ro;
-                const bool vis = row < rows_total && key <= row / H;
+                const bool vis = row < rows_total && row >= first_vis;
                 const float pv = vis ? exp2f(s[rr] * scale_log2 - sL[ro]) : 0.f;
                 p[rr] = pv;
                 ds[rr] = pv * (dp[rr] - sL[kQT + ro]);
@@ -527,8 +552,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
         __syncthreads();
     }
     if (wvalid) {
-        float* okr = dk + (seq0 + key) * HD;
-        float* ovr = dv + (seq0 + key) * HD;
+        const int64_t pslot = ((int64_t)b * slots_per_seq + slot) * kKB + 32 * w + li;
+        float* okr = dk_part + pslot * HD;
+        float* ovr = dv_part + pslot * HD;
 #pragma unroll
         for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
@@ -544,6 +570,47 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     }
 }
 
+// dk[b*T + key] = sum over the chunks of the key's block of the partials, in
+// chunk order (same for dv); one thread per 4 consecutive elements
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_dkv_reduce(const float* __restrict__ dk_part,
+                                                         const float* __restrict__ dv_part,
+                                                         float* __restrict__ dk,
+                                                         float* __restrict__ dv, int B, int T,
+                                                         int H, int chunk_rows,
+                                                         int slots_per_seq) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)B * T * (HD / 4)) return;
+    const int d4 = (int)(idx % (HD / 4));
+    const int64_t tok = idx / (HD / 4);
+    const int b = (int)(tok / T), kk = (int)(tok % T);
+    const int rows_total = T * H;
+    const int kb = kk / kKB, kl = kk % kKB;
+    int slot0 = 0;
+    for (int i = 0; i < kb; ++i) slot0 += kv_chunks(i, H, rows_total, chunk_rows);
+    const int nc = kv_chunks(kb, H, rows_total, chunk_rows);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+    for (int ci = 0; ci < nc; ++ci) {
+        const int64_t off = (((int64_t)b * slots_per_seq + slot0 + ci) * kKB + kl) * HD + d4 * 4;
+        const float4 x = *reinterpret_cast<const float4*>(dk_part + off);
+        const float4 y = *reinterpret_cast<const float4*>(dv_part + off);
+        a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+        c.x += y.x; c.y += y.y; c.z += y.z; c.w += y.w;
+    }
+    *reinterpret_cast<float4*>(dk + tok * HD + d4 * 4) = a;
+    *reinterpret_cast<float4*>(dv + tok * HD + d4 * 4) = c;
+}
+
+int kv_slots_per_seq(int T, int H, int chunk_rows) {
+    const int rows_total = T * H;
+    const int n_kb = (T + kKB - 1) / kKB;
+    int s = 0;
+    for (int kb = 0; kb < n_kb; ++kb) s += kv_chunks(kb, H, rows_total, chunk_rows);
+    return s;
+}
+
+constexpr int kChunkRows = 2048;
+
 template <int HD>
 hipError_t launch_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                       int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, hipStream_t s) {
@@ -557,8 +624,13 @@ hipError_t launch_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
 template <int HD>
 hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                       int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
-                      float* delta, float* dq, float* dk, float* dv, int B, int T, int H,
+                      float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
                       hipStream_t s) {
+    // scratch: delta [B*T*H], then the dK and dV partials
+    float* delta = scratch;
+    const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, kChunkRows) * kKB * HD;
+    float* dk_part = scratch + ceil_div((int64_t)B * T * H, 64) * 64;
+    float* dv_part = dk_part + part;
     hipError_t e = attn_delta<bf16_t>(o, dout, (int64_t)B * T * H, HD, delta, s);
     if (e != hipSuccess) return e;
     const float scale = 1.f / sqrtf((float)HD);
@@ -573,9 +645,15 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
                        ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_kb = (T + kKB - 1) / kKB;
-    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(n_kb * B), dim3(256), 0, s, q, k, v, ldq,
-                       ldkv, dout, lse, delta, dk, dv, B, T, H, scale_log2, scale);
+    const int slots = kv_slots_per_seq(T, H, kChunkRows);
+    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(256), 0, s, q, k, v, ldq,
+                       ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2, scale,
+                       kChunkRows, slots);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n4 = (int64_t)B * T * (HD / 4);
+    hipLaunchKernelGGL(k_attn_dkv_reduce<HD>, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s,
+                       dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots);
     return hipGetLastError();
 }
 
@@ -591,13 +669,19 @@ hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
 
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
-                         float* delta, float* dq, float* dk, float* dv, int B, int T, int H,
+                         float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
                          int hd, hipStream_t s) {
     if (hd == 128)
-        return launch_bwd<128>(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, T, H, s);
+        return launch_bwd<128>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s);
     if (hd == 64)
-        return launch_bwd<64>(q, k, v, ldq, ldkv, o, dout, lse, delta, dq, dk, dv, B, T, H, s);
+        return launch_bwd<64>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s);
     return hipErrorInvalidValue;
+}
+
+size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd) {
+    const int64_t delta = ceil_div((int64_t)B * T * H, 64) * 64;
+    const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, kChunkRows) * kKB * hd;
+    return (size_t)(delta + 2 * part) * sizeof(float);
 }
 
 }  // namespace nc

@@ -14,14 +14,15 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf2f(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
-// round to nearest, ties to even (inputs are finite)
+// fp32 -> bf16, round to nearest, ties to even.  gfx950 converts a pair in
+// one instruction (v_cvt_pk_bf16_f32), which is what these lower to.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t b = __float_as_uint(f);
-    b += 0x7FFFu + ((b >> 16) & 1u);
-    return static_cast<bf16_t>(b >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -56,8 +56,10 @@ hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
                          hipStream_t s);
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
-                         float* delta, float* dq, float* dk, float* dv, int B, int T, int H,
+                         float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
                          int hd, hipStream_t s);
+// bytes of the scratch attn_bwd needs (row sums of dO*O and dK/dV partials)
+size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 // Causal multi-query attention of B sequences of length T with H query heads
 // of width hd and one K/V head.  q: [B*T, H, hd] with token stride ldq;
 // k, v: [B*T, hd] with token stride ldkv; o: [B*T, H*hd]; lse: [B*T*H] fp32.
@@ -65,12 +67,12 @@ template <typename T>
 hipError_t attn_fwd(const T* q, const T* k, const T* v, int64_t ldq,
                     int64_t ldkv, T* o, float* lse, int B, int Tn, int H,
                     int hd, hipStream_t s);
-// Backward: dq [B*T, H, hd], dk, dv [B*T, hd], all fp32; delta is scratch of
-// B*T*H floats.
+// Backward: dq [B*T, H, hd], dk, dv [B*T, hd], all fp32; scratch holds
+// attn_bwd_scratch_bytes(B, T, H, hd) bytes.
 template <typename T>
 hipError_t attn_bwd(const T* q, const T* k, const T* v, int64_t ldq,
                     int64_t ldkv, const T* o, const T* dout, const float* lse,
-                    float* delta, float* dq, float* dk, float* dv, int B,
+                    float* scratch, float* dq, float* dk, float* dv, int B,
                     int Tn, int H, int hd, hipStream_t s);
 
 // ----------------------------------------------------------------- row kernels

@@ -75,25 +75,36 @@ int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
 
 int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
                         const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
-                        const void* o, const void* dout, const float* lse, float* delta,
-                        float* dq, float* dk, float* dv, void* stream) {
+                        const void* o, const void* dout, const float* lse, void* scratch,
+                        size_t scratch_bytes, float* dq, float* dk, float* dv, void* stream) {
     int rc = attn_check(dtype, B, T, H, hd, ldq, ldkv);
     if (rc != NC_OK) return rc;
-    if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv) return NC_ERR_NULL;
+    if (!q || !k || !v || !o || !dout || !lse || !scratch || !dq || !dk || !dv) return NC_ERR_NULL;
     if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al16(dout) || !al16(lse) ||
-        !al16(delta) || !al16(dq) || !al16(dk) || !al16(dv))
+        !al16(scratch) || !al16(dq) || !al16(dk) || !al16(dv))
         return NC_ERR_ALIGN;
+    if (scratch_bytes < nc::attn_bwd_scratch_bytes(B, T, H, hd)) return NC_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    float* sc = static_cast<float*>(scratch);
     if (dtype == NC_F32)
         return ret(nc::attn_bwd<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), ldq, ldkv,
                                        static_cast<const float*>(o),
-                                       static_cast<const float*>(dout), lse, delta, dq, dk, dv,
-                                       B, T, H, hd, s));
+                                       static_cast<const float*>(dout), lse, sc, dq, dk, dv, B, T,
+                                       H, hd, s));
     return ret(nc::attn_bwd<nc::bf16_t>(
         static_cast<const nc::bf16_t*>(q), static_cast<const nc::bf16_t*>(k),
         static_cast<const nc::bf16_t*>(v), ldq, ldkv, static_cast<const nc::bf16_t*>(o),
-        static_cast<const nc::bf16_t*>(dout), lse, delta, dq, dk, dv, B, T, H, hd, s));
+        static_cast<const nc::bf16_t*>(dout), lse, sc, dq, dk, dv, B, T, H, hd, s));
+}
+
+int nc_op_attention_bwd_scratch_bytes(int32_t B, int32_t T, int32_t H, int32_t hd,
+                                      size_t* bytes) {
+    if (!bytes) return NC_ERR_NULL;
+    if (B < 1 || T < 1 || H < 1) return NC_ERR_CONFIG;
+    if (hd != 64 && hd != 128) return NC_ERR_UNSUPPORTED;
+    *bytes = nc::attn_bwd_scratch_bytes(B, T, H, hd);
+    return NC_OK;
 }
 
 int nc_op_softcap_ce(int32_t dtype, int32_t N, int32_t V, int64_t ldz, void* z,

@@ -140,7 +140,7 @@ Plan make_plan(const nc_config& c, bool bwd) {
         p.dn = take((size_t)N * D * 4);
         p.dgu = take((size_t)N * F * es);
         p.dout = take((size_t)N * H * hd * es);
-        p.delta = take((size_t)N * H * 4);
+        p.delta = take(nc::attn_bwd_scratch_bytes(c.batch, c.seq_len, (int)H, (int)hd));
         p.dq = take((size_t)N * H * hd * 4);
         p.dk = take((size_t)N * hd * 4);
         p.dv = take((size_t)N * hd * 4);

@@ -47,12 +47,15 @@ int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
 
 /*
  * Backward of nc_op_attention_fwd for output gradient dout (T [B*T, H*hd]).
- * dq fp32 [B*T, H, hd]; dk, dv fp32 [B*T, hd]; delta: fp32 scratch [B*T*H].
+ * dq fp32 [B*T, H, hd]; dk, dv fp32 [B*T, hd]; scratch: device scratch of at
+ * least nc_op_attention_bwd_scratch_bytes(...) bytes (else NC_ERR_WORKSPACE).
  */
 int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
                         const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
-                        const void* o, const void* dout, const float* lse, float* delta,
-                        float* dq, float* dk, float* dv, void* stream);
+                        const void* o, const void* dout, const float* lse, void* scratch,
+                        size_t scratch_bytes, float* dq, float* dk, float* dv, void* stream);
+int nc_op_attention_bwd_scratch_bytes(int32_t B, int32_t T, int32_t H, int32_t hd,
+                                      size_t* bytes);
 
 /*
  * Softcap + cross-entropy over the rows of z (T [N, ldz], V valid columns,

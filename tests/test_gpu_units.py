@@ -77,7 +77,8 @@ def _pack_qkv(q, k, v):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("Bn,T,H,hd", [(2, 128, 3, 64), (1, 192, 2, 128), (2, 64, 5, 128)])
+@pytest.mark.parametrize("Bn,T,H,hd", [(2, 128, 3, 64), (1, 192, 2, 128), (2, 64, 5, 128),
+                                       (1, 1024, 3, 128)])
 def test_attention_forward_backward(dtype, Bn, T, H, hd):
     torch = require_gpu()
     b = _b()
@@ -109,13 +110,14 @@ def test_attention_forward_backward(dtype, Bn, T, H, hd):
     # backward, with the GPU's own o as the forward output it differentiates
     od = o
     dod = to_dev(do.reshape(Bn * T, H * hd), dtype)
-    delta = torch.empty(Bn * T * H, dtype=torch.float32, device="cuda")
+    nsc = b.nc_op_attention_bwd_scratch_bytes(Bn, T, H, hd)
+    scratch = torch.empty(nsc, dtype=torch.uint8, device="cuda")
     dq = torch.empty((Bn * T, H, hd), dtype=torch.float32, device="cuda")
     dk = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
     dv = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
     b.nc_op_attention_bwd(DT[dtype], Bn, T, H, hd, base, base + H * hd * es,
                           base + (H + 1) * hd * es, ld, ld, od.data_ptr(), dod.data_ptr(),
-                          lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          lse.data_ptr(), scratch.data_ptr(), nsc, dq.data_ptr(), dk.data_ptr(),
                           dv.data_ptr(), stream())
     torch.cuda.synchronize()
     wq, wk, wv = [], [], []
