@@ -13,9 +13,11 @@ causal flop count 6*N_matmul + 6*L*H*hd*(T+1) per token against the bf16
 dense MFMA peak of 2516.6 TFLOP/s.
 
 roofline: the kernel with the largest share of the step (by summed duration)
-from nc_forward_backward_timed, which brackets each launch with HIP events on
-the same stream; achieved = its algorithmic flops (or bytes) per launch over
-its mean launch duration.
+from nc_forward_backward_timed, which brackets each kernel with HIP events on
+the stream it runs on; achieved = its algorithmic flops (or bytes) per launch
+over its mean launch duration.  traffic = HBM bytes per launch measured with
+rocprofv3 counters (profiles/<config>_hbm_traffic.md), null when that record
+does not match the kernel's current sources.
 
 cpu_baseline: the float64 oracle (test infrastructure, unchanged) timed on
 this host for a forward+backward over one sequence of the same workload;
@@ -76,6 +78,34 @@ def timed_kernels(model, params, tok, tgt, reps):
             a[3] += st["bytes"]
     return {k: dict(launches=v[0] / reps, ms=v[1] / reps, flops=v[2] / reps, bytes=v[3] / reps)
             for k, v in acc.items()}
+
+
+def measured_traffic(config_name, label):
+    """HBM bytes per launch of kernel `label` from the committed rocprofv3 PMC
+    summary (FETCH_SIZE and WRITE_SIZE runs scaled by a copy-kernel
+    calibration), or None when there is no record or the kernel's sources
+    have changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{config_name}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get("kernels", {}).get(label)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        fp = os.path.join(ROOT, f)
+        if not os.path.exists(fp):
+            return None
+        with open(fp, "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return float(rec["bytes_per_launch"])
 
 
 def cpu_baseline(cfg):
@@ -163,8 +193,11 @@ def main():
     else:
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
+    traffic = measured_traffic(args.config, dom_name)
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom_name,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": round(dom["bytes"] / max(dom["launches"], 1)),
+                "kernel": dom_name,
                 "launches_per_step": dom["launches"], "mean_launch_ms": round(per_launch_ms, 4),
                 "share_of_step": round(dom["ms"] / total_k, 4)}
     kernels = []

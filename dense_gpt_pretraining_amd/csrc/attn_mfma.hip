@@ -631,7 +631,16 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, kChunkRows) * kKB * HD;
     float* dk_part = scratch + ceil_div((int64_t)B * T * H, 64) * 64;
     float* dv_part = dk_part + part;
-    hipError_t e = attn_delta<bf16_t>(o, dout, (int64_t)B * T * H, HD, delta, s);
+    // algorithmic work of each kernel: causal (row, key) pairs times the
+    // products the kernel forms per pair (2 HD flops each), and the bytes of
+    // its inputs read once and outputs written once
+    const double rows = (double)B * T * H, toks = (double)B * T;
+    const double pairs = (double)B * H * T * (T + 1) / 2.0;
+    const double qo_b = rows * HD * 2.0, kv_b = toks * HD * 2.0;
+    const int slots = kv_slots_per_seq(T, H, kChunkRows);
+    hipError_t e = prof_label("attn_delta", 0, 2 * qo_b + rows * 4.0);
+    if (e != hipSuccess) return e;
+    e = attn_delta<bf16_t>(o, dout, (int64_t)B * T * H, HD, delta, s);
     if (e != hipSuccess) return e;
     const float scale = 1.f / sqrtf((float)HD);
     const float scale_log2 = kLog2e * scale;
@@ -641,15 +650,24 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
         reinterpret_cast<const void*>(k_attn_bwd_dq_mfma<HD>),
         hipFuncAttributeMaxDynamicSharedMemorySize, dq_lds);
     if (attr != hipSuccess) return attr;
+    // dq: S, dP and dQ
+    e = prof_cut("attn_bwd_dq", 3 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows +
+                                                          rows * HD * 4.0);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_bwd_dq_mfma<HD>, dim3(n_rb * B), dim3(256), dq_lds, s, q, k, v, ldq,
                        ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int slots = kv_slots_per_seq(T, H, kChunkRows);
+    // dkv: S, dP, dV and dK; writes one partial per chunk
+    const double part_b = 2.0 * B * slots * kKB * HD * 4.0;
+    e = prof_cut("attn_bwd_dkv", 4 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows + part_b);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(256), 0, s, q, k, v, ldq,
                        ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2, scale,
                        kChunkRows, slots);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = prof_cut("attn_dkv_reduce", 0, part_b + 2.0 * toks * HD * 4.0);
     if (e != hipSuccess) return e;
     const int64_t n4 = (int64_t)B * T * (HD / 4);
     hipLaunchKernelGGL(k_attn_dkv_reduce<HD>, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s,

@@ -553,6 +553,8 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
     }
     if (err != hipSuccess || splits == 1) return err;
     const int64_t n = (int64_t)M * N;
+    err = prof_cut("splitk_reduce", 0, 4.0 * n * (splits + 1 + e.accumulate));
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
                        splitk_ws, splits, M, N, splitk_ld(N), static_cast<float*>(C), ldc,
                        e.accumulate);

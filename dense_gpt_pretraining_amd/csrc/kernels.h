@@ -136,6 +136,15 @@ template <typename T>
 hipError_t zero_elems(T* p, int64_t n, hipStream_t s);
 // records the HIP error behind an NC_ERR_HIP return (read by nc_last_hip_error)
 void note_hip_error(int err);
+
+// Per-kernel timing of the timed step variant.  A launcher that issues more
+// than one kernel names each one: prof_label() renames the segment that is
+// open (call it before the first kernel), prof_cut() closes the open segment
+// at this point of the stream and opens one for the next kernel.  Both are
+// no-ops outside the timed variant.  flops / bytes: the kernel's algorithmic
+// work and HBM bytes.
+hipError_t prof_label(const char* label, double flops, double bytes);
+hipError_t prof_cut(const char* label, double flops, double bytes);
 hipError_t count_bad_ids(const int32_t* a, const int32_t* b, int64_t n, int V,
                          int32_t* n_bad, hipStream_t s);
 

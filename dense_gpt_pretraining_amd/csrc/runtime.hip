@@ -173,7 +173,8 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
         }                                              \
     } while (0)
 
-// Per-launch HIP events for the timed step variant.
+// Per-kernel HIP events for the timed step variant.  A segment runs from one
+// event to the next on the step's stream and covers one kernel.
 struct Prof {
     struct Rec {
         const char* label;
@@ -182,33 +183,51 @@ struct Prof {
     };
     std::vector<Rec> recs;
     hipStream_t s = nullptr;
+    Rec open{nullptr, 0, 0, nullptr, nullptr};
     hipError_t mark(hipEvent_t* ev) {
         hipError_t e = hipEventCreate(ev);
         if (e != hipSuccess) return e;
         return hipEventRecord(*ev, s);
     }
-    hipError_t done(const char* label, double flops, double bytes, hipEvent_t a) {
-        hipEvent_t b = nullptr;
-        hipError_t e = mark(&b);
-        recs.push_back({label, flops, bytes, a, b});
+    hipError_t begin(const char* label, double flops, double bytes) {
+        open = {label, flops, bytes, nullptr, nullptr};
+        return mark(&open.a);
+    }
+    hipError_t close() {
+        hipError_t e = mark(&open.b);
+        recs.push_back(open);
+        open = {nullptr, 0, 0, nullptr, nullptr};
         return e;
     }
+    hipError_t cut(const char* label, double flops, double bytes) {
+        hipEvent_t e = nullptr;
+        hipError_t err = mark(&e);
+        open.b = e;
+        recs.push_back(open);
+        open = {label, flops, bytes, e, nullptr};
+        // the event now ends one segment and starts the next; keep ownership
+        // with the earlier record only
+        return err;
+    }
     ~Prof() {
-        for (auto& r : recs) {
-            if (r.a) (void)hipEventDestroy(r.a);
-            if (r.b) (void)hipEventDestroy(r.b);
+        for (size_t i = 0; i < recs.size(); ++i) {
+            if (recs[i].a && (i == 0 || recs[i].a != recs[i - 1].b)) (void)hipEventDestroy(recs[i].a);
+            if (recs[i].b) (void)hipEventDestroy(recs[i].b);
         }
+        if (open.a && (recs.empty() || open.a != recs.back().b)) (void)hipEventDestroy(open.a);
     }
 };
 
+thread_local Prof* g_prof = nullptr;
+
 // run one launcher; with a profiler, bracket it with events and record its
-// algorithmic flops and HBM bytes under `label`
-#define NC_RUN(label, flops, bytes, expr)                                    \
-    do {                                                                     \
-        hipEvent_t a_ = nullptr;                                             \
-        if (prof) NC_TRY(prof->mark(&a_));                                   \
-        NC_TRY(expr);                                                        \
-        if (prof) NC_TRY(prof->done(label, (double)(flops), (double)(bytes), a_)); \
+// algorithmic flops and HBM bytes under `label` (launchers that issue several
+// kernels split the bracket with prof_cut)
+#define NC_RUN(label, flops, bytes, expr)                                          \
+    do {                                                                           \
+        if (prof) NC_TRY(prof->begin(label, (double)(flops), (double)(bytes)));    \
+        NC_TRY(expr);                                                              \
+        if (prof) NC_TRY(prof->close());                                           \
     } while (0)
 
 template <typename T>
@@ -459,6 +478,20 @@ int check_common(const nc_config* cfg, const void* params, const int32_t* tok,
 
 namespace nc {
 void note_hip_error(int err) { g_last_hip_error = err; }
+
+hipError_t prof_label(const char* label, double flops, double bytes) {
+    if (g_prof && g_prof->open.a) {
+        g_prof->open.label = label;
+        g_prof->open.flops = flops;
+        g_prof->open.bytes = bytes;
+    }
+    return hipSuccess;
+}
+
+hipError_t prof_cut(const char* label, double flops, double bytes) {
+    if (g_prof && g_prof->open.a) return g_prof->cut(label, flops, bytes);
+    return hipSuccess;
+}
 }  // namespace nc
 
 extern "C" {
@@ -562,12 +595,14 @@ int nc_forward_backward_timed(const nc_config* cfg, const void* params, const in
     hipStream_t s = static_cast<hipStream_t>(stream);
     Prof prof;
     prof.s = s;
+    g_prof = &prof;
     if (cfg->dtype == NC_BF16)
         rc = run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, nullptr, grads, ws,
                                   ws_bytes, s, &prof);
     else
         rc = run_step<float>(*cfg, params, tokens, targets, loss, nullptr, grads, ws, ws_bytes, s,
                              &prof);
+    g_prof = nullptr;
     if (rc != NC_OK) return rc;
     NC_TRY(hipStreamSynchronize(s));
     std::vector<nc_kernel_stat> agg;
