@@ -24,7 +24,8 @@ base, architecture list):
 
 Readings where the pages are silent (each also listed in the design notes):
   * norm placement: pre-norm before attention and before the MLP, a final
-    norm before the unembedding, plus the embedding norm ("like Llama");
+    norm before the unembedding, plus the embedding norm (the vpshk page
+    compares the architecture to Llama);
   * rotary pairs element i with element i + hd/2, angle t * base^(-2i/hd),
     positions restart at 0 in every sequence;
   * rotary is applied before QK-norm (they commute exactly);
