@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 
 // ------------------------------------------------------------------ backward: dq
 template <int HD>
-__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
+__global__ __launch_bounds__(256, 1) void k_attn_bwd_dq_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, int B, int T, int H,
