@@ -4,26 +4,38 @@
 // Multi-query attention (architecture list of the nanochat article): all H
 // query heads of a token share one key head and one value head.  The H query
 // vectors of a sequence are read as one [T*H, hd] matrix whose row r is
-// (position t = r / H, head j = r % H); row r may attend to keys tau <= t.
-// A workgroup therefore takes 128 consecutive rows -- every head of ~128/H
-// positions -- and streams the single K/V head through LDS once for all of
-// them, instead of once per head.  The causal bound of a workgroup is set by
-// its last position, so the diagonal waste is one key tile, not a triangle.
+// (position t = r / H, head j = r % H); row r may attend to keys tau <= t,
+// i.e. exactly when r >= tau * H.  A workgroup takes 128 consecutive rows --
+// every head of ~128/H positions -- and streams the single K/V head through
+// LDS once for all of them.
 //
-// Layout trick: scores are computed transposed, S^T = K Q^T, so that the
-// 32x32 accumulator of a wave holds one query row per lane (lane & 31) and 16
-// keys per lane in registers.  The online softmax is then lane-local (plus one
-// exchange with lane ^ 32), and the probabilities are already where the next
-// product O^T = V^T P^T wants its B operand: the 16 keys of one k-step of that
-// product are exactly 8 registers of each of the lanes l and l ^ 32.  Only
-// the A operand (V^T) is read transposed, and that tile is transposed once in
-// registers on its way into LDS.  The backward pass uses the same two layouts.
+// Layouts.  Scores are formed transposed, S^T = K Q^T, so the 32x32
+// accumulator of a wave holds one query row per lane (lane & 31) and 16 keys
+// per lane in registers.  The online softmax is lane-local (plus one exchange
+// with lane ^ 32), and the probabilities are already the B operand of
+// O^T = V^T P^T: the 16 keys of one k step of that product are registers
+// 8h .. 8h+7 of lanes l and l ^ 32, i.e. keys {4g..4g+3, 8+4g..8+4g+3}.  The A
+// operand V^T is fetched from the natural [key][hd] tile with the LDS
+// transpose read (ds_read_b64_tr_b16): within each 16-lane group it hands
+// lane i four consecutive rows of column i, which is exactly four of those
+// keys for one hd column.  The backward kernels use the same two layouts for
+// K^T (dQ), Q^T and dO^T (dK, dV), so no tile is ever transposed in
+// registers or stored twice.
 //
-// Forward: one pass over key tiles with the running max/sum (online softmax),
-// output O and the log-sum-exp per row.
+// Tiles are copied from HBM straight into LDS (global_load_lds_dwordx4, one
+// 16-byte chunk per lane, no registers involved).  Chunk c of tile row r is
+// stored at chunk position c ^ swz(r), which keeps both the row reads (16
+// consecutive rows, one chunk each) and the transpose reads (4 consecutive
+// rows, 4 consecutive chunks) free of bank conflicts.
+//
+// Forward: one pass over key tiles with a running max and sum; the max is
+// only moved (and O, l rescaled) when a row's max grows by more than 2^8, so
+// the rescale is rare -- exact, because O and l always share the same stale
+// max.  Output O and the log-sum-exp per row.
 // Backward: dQ by a row-block kernel that recomputes P from the saved
-// log-sum-exp; dK, dV by a key-block kernel that streams all query rows that
-// can see its keys.  Both keep every sum in a fixed order (no atomics).
+// log-sum-exp; dK, dV by a key-block kernel that streams the query rows that
+// can see its keys, cut into chunks whose partial sums are added in chunk
+// order.  No atomics: the result is deterministic.
 #include "kernels.h"
 
 namespace nc {
@@ -32,34 +44,41 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kKT = 64;     // keys per tile (forward and dq)
-constexpr int kRB = 128;    // query rows per workgroup (forward and dq)
+constexpr int kKT = 64;       // keys per tile (forward and dq)
+constexpr int kRB = 128;      // query rows per workgroup (forward and dq)
+constexpr float kLazy = 8.f;  // log2 headroom before the running max is moved
 
-// element offset in a tile of rows made of NCH 16-byte chunks; chunk index
-// XOR (row & 7) so 8 consecutive rows reading the same chunk hit distinct banks
-template <int NCH>
-__device__ __forceinline__ int rt_off(int row, int ch) {
-    return row * NCH * 8 + ((ch ^ (row & 7 & (NCH - 1))) << 3);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// chunk swizzle of tile row r (depends on r mod 16 only)
+template <int HD>
+__device__ __forceinline__ int swz(int r) {
+    return HD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
-// element offset of element `col` of row `row` in a transposed tile with
-// NCH chunks per row; chunk index XOR ((row >> 1) & (NCH - 1))
-template <int NCH>
-__device__ __forceinline__ int tt_off(int row, int col) {
-    return row * NCH * 8 + ((((col >> 3) ^ ((row >> 1) & (NCH - 1)))) << 3) + (col & 7);
+// byte offset of element `col` of row `row` in a tile of HD-wide rows
+template <int HD>
+__device__ __forceinline__ int toff(int row, int col) {
+    return row * (HD * 2) + (((col >> 3) ^ swz<HD>(row)) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ bf16x8_t lds_b128(const char* p) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+// A operand of a k step over 16 keys (or rows) from a natural tile through
+// two transpose reads; p0 / p1 address the lane's rows 4g.. and 8+4g..
+__device__ __forceinline__ bf16x8_t lds_tr_frag(const char* p0, const char* p1) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return as_bf16x8(make_uint4(a.x, a.y, b.x, b.y));
 }
 
 __device__ __forceinline__ bf16x8_t pack8(const float* x) {
     return as_bf16x8(make_uint4(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
                                 pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])));
-}
-
-// A operand for a k-step over 16 keys (or rows) of a transposed tile: lane
-// supplies row `row`, elements c0 .. c0+3 and c0+8 .. c0+11
-template <int NCH>
-__device__ __forceinline__ bf16x8_t tt_frag(const bf16_t* tile, int row, int c0) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(tile + tt_off<NCH>(row, c0));
-    const uint2 hi = *reinterpret_cast<const uint2*>(tile + tt_off<NCH>(row, c0 + 8));
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 __device__ __forceinline__ f32x16_t zero16() {
@@ -69,17 +88,75 @@ __device__ __forceinline__ f32x16_t zero16() {
     return z;
 }
 
+// 2^x on the hardware exponential unit (no range reduction; -inf -> 0)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// wait for this wave's outstanding global loads (direct LDS copies included)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// barrier without the memory fence of __syncthreads (which would also wait
+// for copies of the next tile still in flight); LDS data it publishes landed
+// through an explicit wait_vmem
+__device__ __forceinline__ void barrier_nofence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Per-lane offsets of the kernels that stream K/V tiles.
+//   ld_src[i]: byte offset, from key row kb of the K (or V) column block, of
+//              the chunk this lane copies with the wave's i-th copy
+//   row_off[kk]: byte offset of the A fragment (row li, k step kk) of a
+//              32-row block of a natural tile
+//   tr_off[db][x]: byte offset, inside a 16-row group, of this lane's
+//              transpose read x (rows 4g.., 8+4g..) for column block db
+// bytes per K or V tile, and direct-copy instructions per wave for one tile
+// (a wave instruction moves 1 KB; four waves share a tile)
+__host__ __device__ constexpr int tile_bytes(int hd) { return kKT * hd * 2; }
+__host__ __device__ constexpr int tile_copies(int hd) { return tile_bytes(hd) / 1024 / 4; }
+template <int HD, int NI>
+__device__ __forceinline__ void tile_lane_offsets(int w, int lane, int64_t ld, int (&ld_src)[NI],
+                                                  int (&row_off)[HD / 16],
+                                                  int (&tr_off)[HD / 32][2]) {
+    constexpr int RPI = 1024 / (HD * 2);   // tile rows per copy instruction
+    const int li = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int row = (w * NI + i) * RPI + lane / (HD / 8);
+        const int p = lane % (HD / 8);
+        ld_src[i] = (int)(row * ld * 2) + ((p ^ swz<HD>(row)) << 4);
+    }
+#pragma unroll
+    for (int kk = 0; kk < HD / 16; ++kk) row_off[kk] = toff<HD>(li, 16 * kk + 8 * g);
+    const int s = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+            tr_off[db][x] = toff<HD>(4 * g + 8 * x + (s >> 2), 32 * db + 16 * half + 4 * (s & 3));
+}
+
+// copy one K tile and one V tile (rows kb.. of the sequence, byte offset
+// `base`) into LDS at sK and sK + tb: this wave's NI instructions of each
+template <int NI>
+__device__ __forceinline__ void copy_kv_tile(const char* kg, const char* vg, int64_t base,
+                                             const int (&ld_src)[NI], char* sK, int tb, int w) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_global_load_lds((const void*)(kg + base + ld_src[i]),
+                                         (lds_void*)(sK + (w * NI + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vg + base + ld_src[i]),
+                                         (lds_void*)(sK + tb + (w * NI + i) * 1024), 16, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------ forward
 template <int HD>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, bf16_t* __restrict__ o, float* __restrict__ lse, int B, int T,
     int H, float scale_log2) {
-    constexpr int KCH = HD / 8;               // 16-byte chunks per K row
-    constexpr int TILE = kKT * HD;            // elements of one K (or V^T) tile
-    constexpr int K_PER = kKT * KCH / 256;    // K chunks staged per thread
-    constexpr int V_BLK = (kKT / 8) * (HD / 8);
-    __shared__ __align__(16) bf16_t sm[2 * 2 * TILE];
+    constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
+    __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
 
     const int rows_total = T * H;
     const int n_rb = (rows_total + kRB - 1) / kRB;
@@ -87,10 +164,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     const int b = (int)(blockIdx.x % B);
     const int64_t seq0 = (int64_t)b * T;
     const int r0 = rb * kRB;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = r0 + 32 * w + li;
     const bool valid = r < rows_total;
-    const int t = valid ? r / H : 0;
+    // a padding row reads no data and sees every key, so it stays finite
+    const int t = valid ? r / H : T - 1;
     const int j = valid ? r % H : 0;
 
     bf16x8_t qf[HD / 16];
@@ -105,108 +184,85 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     const int n_tiles = (last_row / H) / kKT + 1;
     const int w_first = r0 + 32 * w;
     const int tw_max = (w_first < rows_total) ? min(w_first + 31, rows_total - 1) / H : -1;
+    const int tw_min = w_first / H;
+
+    int ld_src[NI], row_off[HD / 16], tr_off[HD / 32][2];
+    tile_lane_offsets<HD, NI>(w, lane, ldkv, ld_src, row_off, tr_off);
+    const char* kg = reinterpret_cast<const char*>(k + seq0 * ldkv);
+    const char* vg = reinterpret_cast<const char*>(v + seq0 * ldkv);
+    auto issue = [&](int kb, int buf) {
+        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, sm + buf * 2 * TB, TB, w);
+    };
 
     f32x16_t oacc[HD / 32];
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) oacc[db] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
 
-    uint4 kreg[K_PER], vreg[8];
-    auto load_tile = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int item = tid + 256 * i, key = item / KCH, ch = item % KCH;
-            kreg[i] = *reinterpret_cast<const uint4*>(k + (seq0 + kb + key) * ldkv + ch * 8);
-        }
-        if (tid < V_BLK) {
-            const int kb8 = tid & 7, db8 = tid >> 3;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                vreg[i] = *reinterpret_cast<const uint4*>(v + (seq0 + kb + kb8 * 8 + i) * ldkv +
-                                                          db8 * 8);
-        }
-    };
-    auto store_tile = [&](int buf) {
-        bf16_t* sK = sm + buf * 2 * TILE;
-        bf16_t* sV = sK + TILE;
-#pragma unroll
-        for (int i = 0; i < K_PER; ++i) {
-            const int item = tid + 256 * i, key = item / KCH, ch = item % KCH;
-            *reinterpret_cast<uint4*>(sK + rt_off<KCH>(key, ch)) = kreg[i];
-        }
-        if (tid < V_BLK) {
-            const int kb8 = tid & 7, db8 = tid >> 3;
-            uint4 tr[8];
-            transpose8x8(vreg, tr);
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint4*>(sV + tt_off<8>(db8 * 8 + c, kb8 * 8)) = tr[c];
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    issue(0, 0);
     for (int it = 0; it < n_tiles; ++it) {
         const int kb = it * kKT;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_tile(kb + kKT);
-        const bf16_t* sK = sm + (it & 1) * 2 * TILE;
-        const bf16_t* sV = sK + TILE;
-        if (kb <= tw_max) {
-            f32x16_t s[2] = {zero16(), zero16()};
+        wait_vmem();
+        barrier_nofence();
+        if (it + 1 < n_tiles) issue(kb + kKT, (it + 1) & 1);
+        const char* sK = sm + (it & 1) * 2 * TB;
+        const char* sV = sK + TB;
+        if (kb > tw_max) continue;
+        f32x16_t s[2] = {zero16(), zero16()};
 #pragma unroll
-            for (int kk = 0; kk < HD / 16; ++kk)
+        for (int kk = 0; kk < HD / 16; ++kk)
 #pragma unroll
-                for (int bi = 0; bi < 2; ++bi) {
-                    const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        sK + rt_off<KCH>(32 * bi + li, 2 * kk + g)));
-                    s[bi] = mfma32(a, qf[kk], s[bi]);
-                }
-            float mx = -INFINITY;
+            for (int bi = 0; bi < 2; ++bi)
+                s[bi] = mfma32(lds_b128(sK + bi * 32 * HD * 2 + row_off[kk]), qf[kk], s[bi]);
+        // keys beyond a row's position exist only on tiles that reach past
+        // the wave's first position
+        if (kb + kKT - 1 > tw_min) {
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int key = kb + 32 * bi + 8 * (rr >> 2) + 4 * g + (rr & 3);
-                    float x = s[bi][rr] * scale_log2;
-                    if (!valid || key > t) x = -INFINITY;
-                    s[bi][rr] = x;
-                    mx = fmaxf(mx, x);
+                    if (key > t) s[bi][rr] = -INFINITY;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            float m_new = fmaxf(m_run, mx);
-            if (m_new == -INFINITY) m_new = 0.f;     // padding rows see no key
-            const float alpha = exp2f(m_run - m_new);
-            float ps = 0.f;
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+        for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const float p = exp2f(s[bi][rr] - m_new);
-                    s[bi][rr] = p;
-                    ps += p;
-                }
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
+            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[bi][rr]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mc = mx * scale_log2;
+        if (__ballot(mc > m_run + kLazy)) {
+            const float mn = fmaxf(m_run, mc);
+            const float alpha = ex2(m_run - mn);
+            l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < HD / 32; ++db) oacc[db] *= alpha;
-#pragma unroll
-            for (int ks = 0; ks < kKT / 16; ++ks) {
-                const int bi = ks >> 1, h = ks & 1;
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] = s[bi][8 * h + e];
-                const bf16x8_t bfrag = pack8(pv);
-#pragma unroll
-                for (int db = 0; db < HD / 32; ++db) {
-                    const bf16x8_t a = tt_frag<8>(sV, 32 * db + li, 32 * bi + 16 * h + 4 * g);
-                    oacc[db] = mfma32(a, bfrag, oacc[db]);
-                }
-            }
+            m_run = mn;
         }
-        if (more) store_tile((it + 1) & 1);
-        __syncthreads();
+        float ps = 0.f;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const float p = ex2(fmaf(s[bi][rr], scale_log2, -m_run));
+                s[bi][rr] = p;
+                ps += p;
+            }
+        l_run += ps;
+#pragma unroll
+        for (int ks = 0; ks < kKT / 16; ++ks) {
+            const int bi = ks >> 1, h = ks & 1;
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv[e] = s[bi][8 * h + e];
+            const bf16x8_t bp = pack8(pv);
+            const char* vb = sV + (32 * bi + 16 * h) * HD * 2;
+#pragma unroll
+            for (int db = 0; db < HD / 32; ++db)
+                oacc[db] = mfma32(lds_tr_frag(vb + tr_off[db][0], vb + tr_off[db][1]), bp,
+                                  oacc[db]);
+        }
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -228,17 +284,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 
 // ------------------------------------------------------------------ backward: dq
 template <int HD>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dq_mfma(
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, int B, int T, int H,
     float scale_log2, float scale) {
-    constexpr int KCH = HD / 8;
-    constexpr int TILE = kKT * HD;
-    constexpr int K_BLK = (kKT / 8) * (HD / 8);      // 8x8 blocks of K (natural + transposed)
-    constexpr int V_PER = kKT * KCH / 256;
-    extern __shared__ __align__(16) unsigned char dq_lds[];
-    bf16_t* sm = reinterpret_cast<bf16_t*>(dq_lds);  // [buf][K | V | K^T]
+    constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
+    __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
 
     const int rows_total = T * H;
     const int n_rb = (rows_total + kRB - 1) / kRB;
@@ -246,10 +298,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq_mfma(
     const int b = (int)(blockIdx.x % B);
     const int64_t seq0 = (int64_t)b * T;
     const int r0 = rb * kRB;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = r0 + 32 * w + li;
     const bool valid = r < rows_total;
-    const int t = valid ? r / H : 0;
+    const int t = valid ? r / H : T - 1;
     const int j = valid ? r % H : 0;
 
     bf16x8_t qf[HD / 16], df[HD / 16];
@@ -264,101 +317,67 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq_mfma(
                            : as_bf16x8(make_uint4(0, 0, 0, 0));
         }
     }
-    const float lse2 = valid ? lse[seq0 * H + r] * kLog2e : 0.f;
+    // p = 2^(s * scale_log2 - lse_row * log2 e)
+    const float nl2 = valid ? -lse[seq0 * H + r] * kLog2e : 0.f;
     const float dl = valid ? delta[seq0 * H + r] : 0.f;
     const int last_row = min(r0 + kRB - 1, rows_total - 1);
     const int n_tiles = (last_row / H) / kKT + 1;
     const int w_first = r0 + 32 * w;
     const int tw_max = (w_first < rows_total) ? min(w_first + 31, rows_total - 1) / H : -1;
+    const int tw_min = w_first / H;
+
+    int ld_src[NI], row_off[HD / 16], tr_off[HD / 32][2];
+    tile_lane_offsets<HD, NI>(w, lane, ldkv, ld_src, row_off, tr_off);
+    const char* kg = reinterpret_cast<const char*>(k + seq0 * ldkv);
+    const char* vg = reinterpret_cast<const char*>(v + seq0 * ldkv);
+    auto issue = [&](int kb, int buf) {
+        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, sm + buf * 2 * TB, TB, w);
+    };
 
     f32x16_t acc[HD / 32];
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) acc[db] = zero16();
 
-    uint4 kreg[8], vreg[V_PER];
-    auto load_tile = [&](int kb) {
-        if (tid < K_BLK) {
-            const int kb8 = tid & 7, db8 = tid >> 3;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                kreg[i] = *reinterpret_cast<const uint4*>(k + (seq0 + kb + kb8 * 8 + i) * ldkv +
-                                                          db8 * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int item = tid + 256 * i, key = item / KCH, ch = item % KCH;
-            vreg[i] = *reinterpret_cast<const uint4*>(v + (seq0 + kb + key) * ldkv + ch * 8);
-        }
-    };
-    auto store_tile = [&](int buf) {
-        bf16_t* sK = sm + buf * 3 * TILE;
-        bf16_t* sV = sK + TILE;
-        bf16_t* sKt = sV + TILE;
-        if (tid < K_BLK) {
-            const int kb8 = tid & 7, db8 = tid >> 3;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(sK + rt_off<KCH>(kb8 * 8 + i, db8)) = kreg[i];
-            uint4 tr[8];
-            transpose8x8(kreg, tr);
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint4*>(sKt + tt_off<8>(db8 * 8 + c, kb8 * 8)) = tr[c];
-        }
-#pragma unroll
-        for (int i = 0; i < V_PER; ++i) {
-            const int item = tid + 256 * i, key = item / KCH, ch = item % KCH;
-            *reinterpret_cast<uint4*>(sV + rt_off<KCH>(key, ch)) = vreg[i];
-        }
-    };
-
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    issue(0, 0);
     for (int it = 0; it < n_tiles; ++it) {
         const int kb = it * kKT;
-        const bool more = it + 1 < n_tiles;
-        if (more) load_tile(kb + kKT);
-        const bf16_t* sK = sm + (it & 1) * 3 * TILE;
-        const bf16_t* sV = sK + TILE;
-        const bf16_t* sKt = sV + TILE;
-        if (kb <= tw_max) {
-            f32x16_t s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+        wait_vmem();
+        barrier_nofence();
+        if (it + 1 < n_tiles) issue(kb + kKT, (it + 1) & 1);
+        const char* sK = sm + (it & 1) * 2 * TB;
+        const char* sV = sK + TB;
+        if (kb > tw_max) continue;
+        const bool diag = kb + kKT - 1 > tw_min;
 #pragma unroll
-            for (int kk = 0; kk < HD / 16; ++kk)
+        for (int bi = 0; bi < 2; ++bi) {
+            f32x16_t s = zero16(), dp = zero16();
+            const char* kr = sK + bi * 32 * HD * 2;
+            const char* vr = sV + bi * 32 * HD * 2;
 #pragma unroll
-                for (int bi = 0; bi < 2; ++bi) {
-                    const bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        sK + rt_off<KCH>(32 * bi + li, 2 * kk + g)));
-                    s[bi] = mfma32(a, qf[kk], s[bi]);
-                    const bf16x8_t av = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        sV + rt_off<KCH>(32 * bi + li, 2 * kk + g)));
-                    dp[bi] = mfma32(av, df[kk], dp[bi]);
-                }
+            for (int kk = 0; kk < HD / 16; ++kk) {
+                s = mfma32(lds_b128(kr + row_off[kk]), qf[kk], s);
+                dp = mfma32(lds_b128(vr + row_off[kk]), df[kk], dp);
+            }
+            float ds[16];
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
+            for (int rr = 0; rr < 16; ++rr) {
+                float p = ex2(fmaf(s[rr], scale_log2, nl2));
+                if (diag) {
                     const int key = kb + 32 * bi + 8 * (rr >> 2) + 4 * g + (rr & 3);
-                    const float p = (valid && key <= t) ? exp2f(s[bi][rr] * scale_log2 - lse2) : 0.f;
-                    s[bi][rr] = p * (dp[bi][rr] - dl);
+                    p = key > t ? 0.f : p;
                 }
+                ds[rr] = p * (dp[rr] - dl);
+            }
 #pragma unroll
-            for (int ks = 0; ks < kKT / 16; ++ks) {
-                const int bi = ks >> 1, h = ks & 1;
-                float dv8[8];
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8_t bd = pack8(&ds[8 * h]);
+                const char* kt = kr + 16 * h * HD * 2;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) dv8[e] = s[bi][8 * h + e];
-                const bf16x8_t bfrag = pack8(dv8);
-#pragma unroll
-                for (int db = 0; db < HD / 32; ++db) {
-                    const bf16x8_t a = tt_frag<8>(sKt, 32 * db + li, 32 * bi + 16 * h + 4 * g);
-                    acc[db] = mfma32(a, bfrag, acc[db]);
-                }
+                for (int db = 0; db < HD / 32; ++db)
+                    acc[db] = mfma32(lds_tr_frag(kt + tr_off[db][0], kt + tr_off[db][1]),
+                                     bd, acc[db]);
             }
         }
-        if (more) store_tile((it + 1) & 1);
-        __syncthreads();
     }
     if (valid) {
         float* out = dq + (seq0 * H + r) * HD;
@@ -376,15 +395,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq_mfma(
 
 // ------------------------------------------------------------------ backward: dk, dv
 constexpr int kKB = 128;   // keys per workgroup (4 waves x 32)
-constexpr int kQT = 32;    // query rows per tile
+constexpr int kQT = 64;    // query rows per tile
 
 // The query rows a key block can see are cut into chunks of `chunk_rows`
 // (a multiple of kQT); chunk c of key block kb of sequence b is one workgroup,
-// which writes its dK, dV sums to partial slot (b, first_slot(kb) + c).  The
-// number of chunks of key block kb is chunks_of(kb).
-__host__ __device__ __forceinline__ int kv_rows_begin(int kb, int H) {
-    return (kb * kKB * H) / kQT * kQT;
-}
+// which writes its dK, dV sums to partial slot (b, first slot of kb + c).
+// Rows before kb * kKB * H see none of the block's keys.
+__host__ __device__ __forceinline__ int kv_rows_begin(int kb, int H) { return kb * kKB * H; }
 __host__ __device__ __forceinline__ int kv_chunks(int kb, int H, int rows_total, int chunk_rows) {
     return (rows_total - kv_rows_begin(kb, H) + chunk_rows - 1) / chunk_rows;
 }
@@ -395,12 +412,11 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dk_part, float* __restrict__ dv_part,
     int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq) {
-    constexpr int KCH = HD / 8;
-    constexpr int QTILE = kQT * HD;                  // elements of one row tile
-    constexpr int BLK = (kQT / 8) * (HD / 8);        // 8x8 blocks of one row tile
-    // per buffer: Q, dO (row tiles), Q^T, dO^T (transposed, kQT columns), lse, delta
-    constexpr int BUF = 4 * QTILE + 2 * kQT * 2;     // in bf16 elements (floats take 2)
-    __shared__ __align__(16) bf16_t sm[2 * BUF];
+    constexpr int TQ = kQT * HD * 2;              // bytes of a Q (or dO) row tile
+    constexpr int RPI = 1024 / (HD * 2);          // tile rows per copy instruction
+    constexpr int NI = TQ / 1024 / 4;             // copy instructions per wave per tile
+    constexpr int BUF = 2 * TQ + 2 * kQT * 4;     // Q | dO | lse | delta
+    __shared__ __align__(1024) char sm[2 * BUF];
 
     const int rows_total = T * H;
     const int n_kb = (T + kKB - 1) / kKB;
@@ -417,7 +433,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     const int r_end = min(r_begin + chunk_rows, rows_total);
     const int64_t seq0 = (int64_t)b * T;
     const int key0 = kbi * kKB;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wkey0 = key0 + 32 * w;
     const bool wvalid = wkey0 < T;
     const int key = wkey0 + li;
@@ -436,120 +453,121 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) { dka[db] = zero16(); dva[db] = zero16(); }
 
-    const int n_qt = (r_end - r_begin + kQT - 1) / kQT;
-
-    uint4 reg[8];
-    float lreg = 0.f;
-    // threads [0, BLK) stage Q blocks, [BLK, 2 BLK) dO blocks, then 2*kQT
-    // threads the lse / delta values
-    auto load_tile = [&](int R0) {
-        if (tid < 2 * BLK) {
-            const int blk = tid % BLK;
-            const bool is_do = tid >= BLK;
-            const int rb8 = blk % (kQT / 8), db8 = blk / (kQT / 8);
-            // position and head of the block's first row; later rows step j
-            const int row0 = R0 + rb8 * 8;
-            int t = row0 / H, j = row0 - t * H;
+    // copy plan: the wave's i-th copy moves tile row (w NI + i) RPI + lane /
+    // (HD/8), chunk position lane % (HD/8).  The Q vector of matrix row r sits
+    // at (t = r / H, head j = r % H) of the qkv buffer; (t, j) of each copied
+    // row advance incrementally by kQT rows per tile.
+    int cp_t[NI], cp_j[NI], cp_c[NI], cp_row[NI];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = row0 + i;
-                if (row < rows_total) {
-                    const bf16_t* src = is_do ? dout + (seq0 * H + row) * HD
-                                              : q + (seq0 + t) * ldq + (int64_t)j * HD;
-                    reg[i] = *reinterpret_cast<const uint4*>(src + db8 * 8);
-                } else {
-                    reg[i] = make_uint4(0, 0, 0, 0);
-                }
-                if (++j == H) { j = 0; ++t; }
-            }
-        } else if (tid < 2 * BLK + 2 * kQT) {
-            const int x = tid - 2 * BLK;
-            const int row = R0 + (x % kQT);
-            const float* src = (x < kQT) ? lse : delta;
-            lreg = (row < rows_total) ? src[seq0 * H + row] : 0.f;
-        }
-    };
-    auto store_tile = [&](int buf) {
-        bf16_t* base = sm + buf * BUF;
-        if (tid < 2 * BLK) {
-            const int blk = tid % BLK;
-            const bool is_do = tid >= BLK;
-            const int rb8 = blk % (kQT / 8), db8 = blk / (kQT / 8);
-            bf16_t* nat = base + (is_do ? QTILE : 0);
-            bf16_t* tr_t = base + 2 * QTILE + (is_do ? QTILE : 0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(nat + rt_off<KCH>(rb8 * 8 + i, db8)) = reg[i];
-            uint4 tr[8];
-            transpose8x8(reg, tr);
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                *reinterpret_cast<uint4*>(tr_t + tt_off<kQT / 8>(db8 * 8 + c, rb8 * 8)) = tr[c];
-        } else if (tid < 2 * BLK + 2 * kQT) {
-            const int x = tid - 2 * BLK;
-            float* lf = reinterpret_cast<float*>(base + 4 * QTILE);
-            lf[x] = (x < kQT) ? lreg * kLog2e : lreg;   // [lse*log2e | delta]
-        }
-    };
-
-    if (n_qt > 0) {
-        load_tile(r_begin);
-        store_tile(0);
+    for (int i = 0; i < NI; ++i) {
+        const int row = (w * NI + i) * RPI + lane / (HD / 8);
+        const int p = lane % (HD / 8);
+        const int rr = r_begin + row;
+        cp_row[i] = row;
+        cp_t[i] = rr / H;
+        cp_j[i] = rr - cp_t[i] * H;
+        cp_c[i] = (p ^ swz<HD>(row)) << 4;
     }
-    __syncthreads();
+    const int step_t = kQT / H, step_j = kQT - step_t * H;
+    const char* qg = reinterpret_cast<const char*>(q + seq0 * ldq);
+    const char* dg = reinterpret_cast<const char*>(dout + seq0 * H * HD);
+    const float* lg = lse + seq0 * H;
+    const float* eg = delta + seq0 * H;
+    auto issue = [&](int R0, int buf) {
+        char* sQ = sm + buf * BUF;
+        char* sD = sQ + TQ;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int64_t qoff = ((int64_t)cp_t[i] * ldq + (int64_t)cp_j[i] * HD) * 2 + cp_c[i];
+            const int64_t doff = (int64_t)(R0 + cp_row[i]) * HD * 2 + cp_c[i];
+            __builtin_amdgcn_global_load_lds(qg + qoff, (lds_void*)(sQ + (w * NI + i) * 1024), 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds(dg + doff, (lds_void*)(sD + (w * NI + i) * 1024), 16,
+                                             0, 0);
+            cp_j[i] += step_j;
+            cp_t[i] += step_t;
+            if (cp_j[i] >= H) { cp_j[i] -= H; cp_t[i] += 1; }
+        }
+        // one wave copies the tile's log-sum-exp values, another its deltas
+        if (w == 0)
+            __builtin_amdgcn_global_load_lds(lg + R0 + lane, (lds_void*)(sD + TQ), 4, 0, 0);
+        else if (w == 1)
+            __builtin_amdgcn_global_load_lds(eg + R0 + lane, (lds_void*)(sD + TQ + kQT * 4), 4, 0,
+                                             0);
+    };
+    int row_off[HD / 16], tr_off[HD / 32][2];
+    {
+        const int s = lane & 15, half = (lane >> 4) & 1;
+#pragma unroll
+        for (int kk = 0; kk < HD / 16; ++kk) row_off[kk] = toff<HD>(li, 16 * kk + 8 * g);
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                tr_off[db][x] = toff<HD>(4 * g + 8 * x + (s >> 2),
+                                         32 * db + 16 * half + 4 * (s & 3));
+    }
+
+    const int n_qt = (r_end - r_begin) / kQT;
+    const int first_vis = key * H;            // first row that sees this lane's key
+    const int w_first_vis = wkey0 * H;        // first row that sees the wave's first key
+    const int w_all_vis = (wkey0 + 31) * H;   // from here on every row sees every key
+    if (n_qt > 0) issue(r_begin, 0);
     for (int it = 0; it < n_qt; ++it) {
         const int R0 = r_begin + it * kQT;
-        const bool more = it + 1 < n_qt;
-        if (more) load_tile(R0 + kQT);
-        const bf16_t* base = sm + (it & 1) * BUF;
-        const bf16_t* sQ = base;
-        const bf16_t* sD = base + QTILE;
-        const bf16_t* sQt = base + 2 * QTILE;
-        const bf16_t* sDt = base + 3 * QTILE;
-        const float* sL = reinterpret_cast<const float*>(base + 4 * QTILE);
-        // rows of this tile reach keys up to their position; skip the tile if
-        // even its last row precedes this wave's first key
-        // some row of the tile sees this wave's first key iff its last row
-        // r satisfies r >= wkey0 * H
-        if (wvalid && min(R0 + kQT - 1, rows_total - 1) >= wkey0 * H) {
+        wait_vmem();
+        barrier_nofence();
+        if (it + 1 < n_qt) issue(R0 + kQT, (it + 1) & 1);
+        const char* sQ = sm + (it & 1) * BUF;
+        const char* sD = sQ + TQ;
+        const float* sL = reinterpret_cast<const float*>(sD + TQ);
+        if (!wvalid) continue;
+#pragma unroll
+        for (int qb = 0; qb < kQT / 32; ++qb) {
+            const int rb0 = R0 + 32 * qb;
+            if (rb0 + 31 < w_first_vis) continue;       // no row of the block sees a key
+            const char* qr = sQ + qb * 32 * HD * 2;
+            const char* dr = sD + qb * 32 * HD * 2;
             f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
-                const bf16x8_t aq = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    sQ + rt_off<KCH>(li, 2 * kk + g)));
-                s = mfma32(aq, kf[kk], s);
-                const bf16x8_t ad = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    sD + rt_off<KCH>(li, 2 * kk + g)));
-                dp = mfma32(ad, vf[kk], dp);
+                s = mfma32(lds_b128(qr + row_off[kk]), kf[kk], s);
+                dp = mfma32(lds_b128(dr + row_off[kk]), vf[kk], dp);
             }
-            // lane holds key `key`; register rr holds row R0 + 8(rr/4) + 4g + rr%4.
-            // Row r sits at position r / H, and key <= r / H exactly when r >= key * H.
+            // lane holds key `key`; register rr holds row rb0 + 8(rr/4) + 4g + rr%4
+            const bool partial = rb0 < w_all_vis;
             float p[16], ds[16];
-            const int first_vis = key * H;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int ro = 8 * (rr >> 2) + 4 * g + (rr & 3);
-                const int row = R0 + ro;
-                const bool vis = row < rows_total && row >= first_vis;
-                const float pv = vis ? exp2f(s[rr] * scale_log2 - sL[ro]) : 0.f;
-                p[rr] = pv;
-                ds[rr] = pv * (dp[rr] - sL[kQT + ro]);
+            for (int m = 0; m < 4; ++m) {
+                const int ro = 32 * qb + 8 * m + 4 * g;
+                const float4 l4 = *reinterpret_cast<const float4*>(sL + ro);
+                const float4 d4 = *reinterpret_cast<const float4*>(sL + kQT + ro);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = 4 * m + e;
+                    float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
+                    if (partial) pv = (rb0 + 8 * m + 4 * g + e >= first_vis) ? pv : 0.f;
+                    p[rr] = pv;
+                    ds[rr] = pv * (dp[rr] - dv4[e]);
+                }
             }
 #pragma unroll
-            for (int ks = 0; ks < kQT / 16; ++ks) {
-                const bf16x8_t bp = pack8(p + 8 * ks);
-                const bf16x8_t bd = pack8(ds + 8 * ks);
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8_t bp = pack8(&p[8 * h]);
+                const bf16x8_t bd = pack8(&ds[8 * h]);
+                const char* dt = dr + 16 * h * HD * 2;
+                const char* qt = qr + 16 * h * HD * 2;
 #pragma unroll
                 for (int db = 0; db < HD / 32; ++db) {
-                    const bf16x8_t ado = tt_frag<kQT / 8>(sDt, 32 * db + li, 16 * ks + 4 * g);
-                    dva[db] = mfma32(ado, bp, dva[db]);
-                    const bf16x8_t aqt = tt_frag<kQT / 8>(sQt, 32 * db + li, 16 * ks + 4 * g);
-                    dka[db] = mfma32(aqt, bd, dka[db]);
+                    dva[db] = mfma32(lds_tr_frag(dt + tr_off[db][0], dt + tr_off[db][1]), bp,
+                                     dva[db]);
+                    dka[db] = mfma32(lds_tr_frag(qt + tr_off[db][0], qt + tr_off[db][1]), bd,
+                                     dka[db]);
                 }
             }
         }
-        if (more) store_tile((it + 1) & 1);
-        __syncthreads();
     }
     if (wvalid) {
         const int64_t pslot = ((int64_t)b * slots_per_seq + slot) * kKB + 32 * w + li;
@@ -610,6 +628,7 @@ int kv_slots_per_seq(int T, int H, int chunk_rows) {
 }
 
 constexpr int kChunkRows = 2048;
+static_assert(kChunkRows % kQT == 0, "chunks hold whole row tiles");
 
 template <int HD>
 hipError_t launch_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
@@ -628,7 +647,8 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
                       hipStream_t s) {
     // scratch: delta [B*T*H], then the dK and dV partials
     float* delta = scratch;
-    const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, kChunkRows) * kKB * HD;
+    const int slots = kv_slots_per_seq(T, H, kChunkRows);
+    const int64_t part = (int64_t)B * slots * kKB * HD;
     float* dk_part = scratch + ceil_div((int64_t)B * T * H, 64) * 64;
     float* dv_part = dk_part + part;
     // algorithmic work of each kernel: causal (row, key) pairs times the
@@ -637,7 +657,6 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const double rows = (double)B * T * H, toks = (double)B * T;
     const double pairs = (double)B * H * T * (T + 1) / 2.0;
     const double qo_b = rows * HD * 2.0, kv_b = toks * HD * 2.0;
-    const int slots = kv_slots_per_seq(T, H, kChunkRows);
     hipError_t e = prof_label("attn_delta", 0, 2 * qo_b + rows * 4.0);
     if (e != hipSuccess) return e;
     e = attn_delta<bf16_t>(o, dout, (int64_t)B * T * H, HD, delta, s);
@@ -645,16 +664,11 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const float scale = 1.f / sqrtf((float)HD);
     const float scale_log2 = kLog2e * scale;
     const int n_rb = (T * H + kRB - 1) / kRB;
-    constexpr int dq_lds = 2 * 3 * kKT * HD * 2;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(k_attn_bwd_dq_mfma<HD>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, dq_lds);
-    if (attr != hipSuccess) return attr;
     // dq: S, dP and dQ
     e = prof_cut("attn_bwd_dq", 3 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows +
                                                           rows * HD * 4.0);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_bwd_dq_mfma<HD>, dim3(n_rb * B), dim3(256), dq_lds, s, q, k, v, ldq,
+    hipLaunchKernelGGL(k_attn_bwd_dq_mfma<HD>, dim3(n_rb * B), dim3(256), 0, s, q, k, v, ldq,
                        ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
