@@ -12,13 +12,15 @@
 // LDS buffers with an XOR swizzle of the 16-byte chunks of each row, so
 // fragment reads of 8 or 16 consecutive rows at one logical chunk hit
 // distinct banks (the bank-conflict counter reads zero).
-//   k-major operands go straight from global memory into LDS
+//   Both operands go straight from global memory into LDS
 //   (global_load_lds_dwordx4, no staging registers); the loads of tile k+1
 //   are in flight while tile k is multiplied, and the fragments of k step
 //   s+1 are read while the matrix instructions of step s issue.
-//   mn-major operands (the weight-gradient layout) are loaded as 8 x 8 blocks
-//   into registers and transposed before the LDS write, so fragment reads are
-//   the same 16-byte reads for every layout.
+//   k-major tiles are stored 256 rows x 64 k and a fragment is one 16-byte
+//   read; mn-major tiles (the weight-gradient layout) are stored as they lie
+//   in memory, 64 k x 256 rows, and a fragment (8 consecutive k of one row)
+//   is two LDS transpose reads (ds_read_b64_tr_b16), so no layout is ever
+//   transposed in registers.
 // The MFMA "A" side takes the n rows and the "B" side the m rows, which puts
 // 4 consecutive n of one row m in each lane's accumulator registers: the
 // epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
@@ -170,36 +172,60 @@ __device__ __forceinline__ void kmaj_issue(const bf16_t* tile_base, const KmajLo
     }
 }
 
-template <bool KMAJ>
-__device__ __forceinline__ void mn_load(const bf16_t* __restrict__ P, int64_t ld, int rows,
-                                        int K, int r0, int k0, uint4* reg, int half) {
-    const int tid = threadIdx.x;
-    if ((tid >> 8) != half) return;
-    const int t = tid & 255;
-    const int r = r0 + (t & 31) * 8;
-    const int kb = k0 + (t >> 5) * 8;
+// mn-major operand P(r, k) = P[k * ld + r]: the tile is stored as it lies in
+// memory, 64 k rows of 256 r (512 bytes, 32 chunks), chunk c of k row kr at
+// chunk position c ^ ((kr & 3) << 2).  Copy instruction i of wave w fills k
+// rows 2 (8 i + w) and 2 (8 i + w) + 1; lane l takes row + (l >> 5), chunk
+// position l & 31.  Chunks past `rows` are redirected to column 0 of the
+// same k row (their products land in outputs that are never stored).
+// Requires k0 + 64 <= K.
+struct MnLoads {
+    int off[4];   // byte offsets of this lane's four chunks from element (k0, r0)
+};
+
+__device__ __forceinline__ MnLoads mn_offsets(int64_t ld, int rows, int r0, int w, int lane) {
+    MnLoads L;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int k = kb + i;
-        if (r < rows && k < K)
-            reg[i] = *reinterpret_cast<const uint4*>(P + (int64_t)k * ld + r);
-        else
-            reg[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+        const int kr = 2 * (8 * i + w) + (lane >> 5);
+        const int c = (lane & 31) ^ ((kr & 3) << 2);
+        const int col = r0 + 8 * c < rows ? 8 * c : -r0;
+        L.off[i] = (int)(((int64_t)kr * ld + col) * 2);
+    }
+    return L;
+}
+
+__device__ __forceinline__ void mn_issue(const bf16_t* tile_base, const MnLoads& L, bf16_t* T,
+                                         int w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const char* g = reinterpret_cast<const char*>(tile_base) + L.off[i];
+        __builtin_amdgcn_global_load_lds(
+            (const void*)g, (__attribute__((address_space(3))) void*)(T + (i * 8 + w) * 512), 16,
+            0, 0);
     }
 }
 
-__device__ __forceinline__ void tile_store_mn(bf16_t* T, const uint4* reg, int half) {
-    const int tid = threadIdx.x;
-    if ((tid >> 8) != half) return;
-    const int t = tid & 255;
-    uint4 tr[8];
-    transpose8x8(reg, tr);
-    const int ch = t >> 5;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int r = (t & 31) * 8 + c;
-        *reinterpret_cast<uint4*>(T + swz(r, ch)) = tr[c];
-    }
+// byte offset, in an mn-major tile, of this lane's first transpose read for
+// the 32-row block starting at r (k step 0): rows k = 8 g + (s >> 2), columns
+// r + 16 half + 4 (s & 3), s = lane & 15.  The second read of a fragment is
+// 4 k rows further; k step ks adds 16 ks rows.  The chunk swizzle depends
+// on k & 3 = s >> 2 only, so these offsets hold for every k step.
+__device__ __forceinline__ int mn_frag_off(int r, int lane) {
+    const int s = lane & 15, half = (lane >> 4) & 1, g = lane >> 5;
+    const int kr = 8 * g + (s >> 2);
+    const int col = r + 16 * half + 4 * (s & 3);
+    return kr * 512 + ((((col >> 3) ^ ((kr & 3) << 2))) << 4) + ((col & 7) << 1);
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+// 8 consecutive k of one row from an mn-major tile: two transpose reads
+__device__ __forceinline__ bf16x8_t mn_frag(const char* p) {
+    typedef __attribute__((address_space(3))) v4i16_t lds4;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4*)(p));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds4*)(p + 4 * 512));
+    const uint2 x = __builtin_bit_cast(uint2, lo), y = __builtin_bit_cast(uint2, hi);
+    return as_bf16x8(make_uint4(x.x, x.y, y.x, y.y));
 }
 
 // wait until this thread's direct global->LDS loads have landed
@@ -267,31 +293,10 @@ __device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, 
 
 // 512 threads: wave w owns m rows wm*64 .. +63 (wm = w & 3) and n rows
 // wn*128 .. +127 (wn = w >> 2) of the 256 x 256 tile: 2 x 4 accumulator blocks.
-// A fragment row 32 i + (lane & 31) of a 32-aligned block has swizzle
-// f0 ^ 4 (i & 1) with f0 that of (lane & 31), so the chunk offsets of the 4
-// k steps for the two parities are precomputed per lane (foff) and every
-// fragment read is base + constant.
-__device__ __forceinline__ void mma_tile(const bf16_t* sA, const bf16_t* sB, f32x16_t (&acc)[4][2],
-                                         const int (&foff)[2][4], int wm, int wn, int lane) {
-    const int rowoff = (lane & 31) * kTK;
-#pragma unroll
-    for (int ks = 0; ks < kTK / 16; ++ks) {
-        bf16x8_t fa[4], fb[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            fb[j] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]));
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
-    }
-}
-
+// In a k-major tile, fragment row 32 i + (lane & 31) of a 32-aligned block
+// has swizzle f0 ^ 4 (i & 1) with f0 that of (lane & 31), so the chunk
+// offsets of the 4 k steps for the two parities are precomputed per lane
+// (foff) and every fragment read is base + constant.
 template <bool AK, bool BK, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, int k_per_split,
                                                            const bf16_t* __restrict__ A,
@@ -343,29 +348,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             for (int ks = 0; ks < 4; ++ks) foff[p][ks] = ((2 * ks + fch) ^ f0 ^ (4 * p)) << 3;
     }
 
+    // both operands stream straight into LDS; the two layouts differ only in
+    // the copy offsets and in how a fragment is read (one 16-byte row read
+    // for k-major, two transpose reads for mn-major)
     KmajLoads la, lb;
+    MnLoads ma, mb;
     if (AK) la = kmaj_offsets(lda, M, m0, wave, lane);
+    else ma = mn_offsets(lda, M, m0, wave, lane);
     if (BK) lb = kmaj_offsets(ldb, N, n0, wave, lane);
-    uint4 ra[8], rb[8];
+    else mb = mn_offsets(ldb, N, n0, wave, lane);
+    int tra[2], trb[4];
+    if (!AK)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) tra[j] = mn_frag_off(wm * 64 + j * 32, lane);
+    if (!BK)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) trb[i] = mn_frag_off(wn * 128 + i * 32, lane);
     const int nk = (ke - kb + kTK - 1) / kTK;
     auto issue = [&](int kt, bf16_t* buf) {
         const int k0 = kb + kt * kTK;
         if (AK) kmaj_issue(A + (int64_t)m0 * lda + k0, la, buf, wave);
-        else mn_load<false>(A, lda, M, ke, m0, k0, ra, 0);
+        else mn_issue(A + (int64_t)k0 * lda + m0, ma, buf, wave);
         if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, buf + kTileElems, wave);
-        else mn_load<false>(B, ldb, N, ke, n0, k0, rb, 1);
-    };
-    auto finish = [&](bf16_t* buf) {
-        if (!AK) tile_store_mn(buf, ra, 0);
-        if (!BK) tile_store_mn(buf + kTileElems, rb, 1);
-        if (AK || BK) wait_vmem();
+        else mn_issue(B + (int64_t)k0 * ldb + n0, mb, buf + kTileElems, wave);
     };
     if (nk > 0) {
         issue(0, lds0);
-        finish(lds0);
+        wait_vmem();
     }
     __syncthreads();
-    if (AK && BK) {
+    {
         // fragments of k step ks+1 (or of the next tile's first step) are
         // read while the 8 matrix instructions of step ks issue
         const int rowoff = (lane & 31) * kTK;
@@ -375,12 +387,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             const bf16_t* sB = buf + kTileElems;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[set][i] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]));
+                fa[set][i] = BK ? as_bf16x8(*reinterpret_cast<const uint4*>(
+                                      sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]))
+                                : mn_frag(reinterpret_cast<const char*>(sB) + trb[i] + ks * 16 * 512);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                fb[set][j] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]));
+                fb[set][j] = AK ? as_bf16x8(*reinterpret_cast<const uint4*>(
+                                      sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]))
+                                : mn_frag(reinterpret_cast<const char*>(sA) + tra[j] + ks * 16 * 512);
         };
         for (int kt = 0; kt < nk; ++kt) {
             bf16_t* cur = (kt & 1) ? lds1 : lds0;
@@ -407,40 +421,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-    } else {
-        for (int kt = 0; kt < nk; ++kt) {
-            bf16_t* cur = (kt & 1) ? lds1 : lds0;
-            bf16_t* nxt = (kt & 1) ? lds0 : lds1;
-            const bool more = kt + 1 < nk;
-            if (more) issue(kt + 1, nxt);
-            mma_tile(cur, cur + kTileElems, acc, foff, wm, wn, lane);
-            if (more) finish(nxt);
-            __syncthreads();
-        }
     }
 
-    // epilogue: lane holds m = m0 + wm*64 + 32 j + (lane & 31) and, for
-    // register group g, n = n0 + wn*128 + 32 i + 8 g + 4 (lane >> 5) + 0..3
+    // epilogue, staged through LDS so that global reads and writes are whole
+    // rows: lane holds m = m0 + wm*64 + 32 j + (lane & 31) and, for register
+    // group q of block i, n = n0 + wn*128 + 32 i + 8 q + 4 (lane >> 5) + 0..3.
+    // For each j the wave parks its 32 x 128 fp32 block in its own 16 KB of
+    // LDS (16-byte chunk c of row r at chunk position c ^ r), then reads it
+    // back two rows per instruction: lane l takes row 2 t + (l >> 5), columns
+    // 4 (l & 31) .. +3, so 32 lanes cover one row's 128 columns contiguously.
+    __syncthreads();   // every wave is done with the last k tile
+    float* stage = reinterpret_cast<float*>(wave < 4 ? lds0 : lds1) + (wave & 3) * 4096;
     const bool full_n = n0 + kTN <= N;
+    const int li = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int64_t m = m0 + wm * 64 + 32 * j + (lane & 31);
-        if (m >= M) continue;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int64_t n = n0 + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
-                const float a[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                    acc[i][j][4 * g + 3]};
-                if (full_n || n + 3 < N) {
-                    epi_vec4<MODE>(e, C, m * ldc + n, m, a[0], a[1], a[2], a[3]);
-                } else {
-                    for (int q = 0; q < 4; ++q)
-                        if (n + q < N) epi_store1<bf16_t>(e, C, ldc, m, n + q, a[q]);
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int c = 8 * i + 2 * q + hi;
+                *reinterpret_cast<float4*>(stage + li * 128 + ((c ^ li) << 2)) =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]);
+            }
+        __syncthreads();
+        const int64_t n = n0 + wn * 128 + 4 * li;
+#pragma unroll 4
+        for (int t = 0; t < 16; ++t) {
+            const int row = 2 * t + hi;
+            const float4 v = *reinterpret_cast<const float4*>(stage + row * 128 + ((li ^ row) << 2));
+            const int64_t m = m0 + wm * 64 + 32 * j + row;
+            if (m >= M) continue;
+            if (full_n || n + 3 < N) {
+                epi_vec4<MODE>(e, C, m * ldc + n, m, v.x, v.y, v.z, v.w);
+            } else {
+                const float a[4] = {v.x, v.y, v.z, v.w};
+                for (int q = 0; q < 4; ++q)
+                    if (n + q < N) epi_store1<bf16_t>(e, C, ldc, m, n + q, a[q]);
             }
         }
+        if (j == 0) __syncthreads();
     }
 }
 
@@ -456,13 +477,22 @@ __global__ void k_splitk_reduce(const float* __restrict__ part, int splits, int 
     out[m * ldc + n] = s;
 }
 
+// k-split of a GEMM with few output tiles: the split count s that minimises
+// the modelled time rounds(s) * (k per split + c), rounds(s) = workgroup
+// waves of tiles * s over the 256 compute units and c ~ the fixed cost of a
+// workgroup (prologue, epilogue) in k units.  Each split keeps >= 512 of k.
 int choose_splits(int M, int N, int K) {
-    const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
-    int splits = 1;
-    // aim for at least 2 workgroups per compute unit (256 CUs) while each
-    // split keeps >= 1024 of k
-    while (tiles * splits < 512 && K / (splits * 2) >= 1024) splits *= 2;
-    return splits;
+    const int64_t tiles = ceil_div(M, kTM) * ceil_div(N, kTN);
+    constexpr int64_t kCUs = 256, kFixed = 384;
+    int best = 1;
+    int64_t best_cost = ceil_div(tiles, kCUs) * ((int64_t)K + kFixed);
+    for (int s = 2; s <= 32; ++s) {
+        const int64_t kper = ceil_div(ceil_div(K, s), kTK) * kTK;
+        if (kper < 512 || ceil_div(K, kper) < s) break;
+        const int64_t cost = ceil_div(tiles * s, kCUs) * (kper + kFixed);
+        if (cost < best_cost) { best = s; best_cost = cost; }
+    }
+    return best;
 }
 
 template <bool AK, bool BK, int MODE>

@@ -28,7 +28,9 @@ def _b():
     (300, 520, 192, True),      # several 256 tiles, ragged m and n tails
     (256, 256, 64, True),       # exactly one tile
     (1, 8, 64, True),           # degenerate m, n
-    (264, 136, 1000, False),    # mn-major operands (weight-gradient layout), ragged k
+    (264, 136, 1024, False),    # mn-major operands (weight-gradient layout), ragged m, n
+    (300, 520, 192, False),     # mn-major, several tiles
+    (1, 8, 64, False),          # mn-major, degenerate m, n
     (512, 768, 4096, False),    # long k: split over the k loop
 ])
 def test_matmul(dtype, M, N, K, kmajor):
