@@ -22,8 +22,8 @@
 // K^T (dQ), Q^T and dO^T (dK, dV), so no tile is ever transposed in
 // registers or stored twice.
 //
-// Tiles are copied from HBM straight into LDS (global_load_lds_dwordx4, one
-// 16-byte chunk per lane, no registers involved).  Chunk c of tile row r is
+// Tiles are copied from HBM straight into LDS (buffer loads with the LDS bit,
+// one 16-byte chunk per lane, no registers involved).  Chunk c of tile row r is
 // stored at chunk position c ^ swz(r), which keeps both the row reads (16
 // consecutive rows, one chunk each) and the transpose reads (4 consecutive
 // rows, 4 consecutive chunks) free of bank conflicts.
@@ -50,7 +50,6 @@ constexpr float kLazy = 8.f;  // log2 headroom before the running max is moved
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // chunk swizzle of tile row r (depends on r mod 16 only)
 template <int HD>
@@ -140,12 +139,11 @@ __device__ __forceinline__ void tile_lane_offsets(int w, int lane, int64_t ld, i
 template <int NI>
 __device__ __forceinline__ void copy_kv_tile(const char* kg, const char* vg, int64_t base,
                                              const int (&ld_src)[NI], char* sK, int tb, int w) {
+    const buf_rsrc_t rk = make_rsrc(kg + base), rv = make_rsrc(vg + base);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        __builtin_amdgcn_global_load_lds((const void*)(kg + base + ld_src[i]),
-                                         (lds_void*)(sK + (w * NI + i) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vg + base + ld_src[i]),
-                                         (lds_void*)(sK + tb + (w * NI + i) * 1024), 16, 0, 0);
+        lds_copy<16>(rk, ld_src[i], sK + (w * NI + i) * 1024);
+        lds_copy<16>(rv, ld_src[i], sK + tb + (w * NI + i) * 1024);
     }
 }
 
@@ -473,27 +471,30 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     const char* dg = reinterpret_cast<const char*>(dout + seq0 * H * HD);
     const float* lg = lse + seq0 * H;
     const float* eg = delta + seq0 * H;
+    // the Q rows of a tile span under kQT / H + 2 positions of the qkv buffer,
+    // so offsets from the position of the tile's first row stay small
     auto issue = [&](int R0, int buf) {
         char* sQ = sm + buf * BUF;
         char* sD = sQ + TQ;
+        const int t0 = R0 / H;
+        const buf_rsrc_t rq = make_rsrc(qg + (int64_t)t0 * ldq * 2);
+        const buf_rsrc_t rd = make_rsrc(dg + (int64_t)R0 * HD * 2);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int64_t qoff = ((int64_t)cp_t[i] * ldq + (int64_t)cp_j[i] * HD) * 2 + cp_c[i];
-            const int64_t doff = (int64_t)(R0 + cp_row[i]) * HD * 2 + cp_c[i];
-            __builtin_amdgcn_global_load_lds(qg + qoff, (lds_void*)(sQ + (w * NI + i) * 1024), 16,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds(dg + doff, (lds_void*)(sD + (w * NI + i) * 1024), 16,
-                                             0, 0);
+            const int qoff = (int)(((int64_t)(cp_t[i] - t0) * ldq + (int64_t)cp_j[i] * HD) * 2) +
+                             cp_c[i];
+            const int doff = cp_row[i] * HD * 2 + cp_c[i];
+            lds_copy<16>(rq, qoff, sQ + (w * NI + i) * 1024);
+            lds_copy<16>(rd, doff, sD + (w * NI + i) * 1024);
             cp_j[i] += step_j;
             cp_t[i] += step_t;
             if (cp_j[i] >= H) { cp_j[i] -= H; cp_t[i] += 1; }
         }
         // one wave copies the tile's log-sum-exp values, another its deltas
         if (w == 0)
-            __builtin_amdgcn_global_load_lds(lg + R0 + lane, (lds_void*)(sD + TQ), 4, 0, 0);
+            lds_copy<4>(make_rsrc(lg + R0), lane * 4, sD + TQ);
         else if (w == 1)
-            __builtin_amdgcn_global_load_lds(eg + R0 + lane, (lds_void*)(sD + TQ + kQT * 4), 4, 0,
-                                             0);
+            lds_copy<4>(make_rsrc(eg + R0), lane * 4, sD + TQ + kQT * 4);
     };
     int row_off[HD / 16], tr_off[HD / 32][2];
     {

@@ -123,6 +123,27 @@ __device__ __forceinline__ float tanh_f(float x) {
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ------------------------------------------------------------ HBM -> LDS copies
+// A buffer resource over [base, base + 2 GiB) with no format conversion; the
+// copies below go through it as MUBUF loads with the LDS bit, which the
+// compiler tracks as plain vector-memory loads (its flat-instruction path
+// would also flush the LDS counter at every later LDS dependency).
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                             0x00020000);
+}
+// lane l copies `bytes` (4 or 16) from base + voff to LDS at lds + l * bytes;
+// `lds` must be the same for every lane of the wave
+template <int BYTES>
+__device__ __forceinline__ void lds_copy(buf_rsrc_t r, int voff, void* lds) {
+    auto* l = (__attribute__((address_space(3))) void*)lds;
+    if constexpr (BYTES == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 4, voff, 0, 0, 0);
+}
+
 // ------------------------------------------------------------ matrix cores
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

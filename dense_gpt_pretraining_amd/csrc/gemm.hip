@@ -13,7 +13,7 @@
 // fragment reads of 8 or 16 consecutive rows at one logical chunk hit
 // distinct banks (the bank-conflict counter reads zero).
 //   Both operands go straight from global memory into LDS
-//   (global_load_lds_dwordx4, no staging registers); the loads of tile k+1
+//   (buffer loads with the LDS bit, no staging registers); the loads of tile k+1
 //   are in flight while tile k is multiplied, and the fragments of k step
 //   s+1 are read while the matrix instructions of step s issue.
 //   k-major tiles are stored 256 rows x 64 k and a fragment is one 16-byte
@@ -135,7 +135,7 @@ __device__ __forceinline__ int swz_f(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz(int row, int ch) { return row * kTK + ((ch ^ swz_f(row)) << 3); }
 
 // Stage one 256-row x 64-k operand tile into LDS.
-//   k-major: straight from global memory into LDS (global_load_lds_dwordx4).
+//   k-major: straight from global memory into LDS (buffer load, LDS bit).
 //     Wave w's instruction i fills the 64 consecutive 16-byte LDS slots of
 //     rows 64 i + 8 w .. +7, so lane l holds row 64 i + 8 w + (l >> 3) at
 //     physical chunk l & 7, i.e. logical chunk (l & 7) ^ (l >> 3) ^ w under
@@ -163,22 +163,19 @@ __device__ __forceinline__ KmajLoads kmaj_offsets(int64_t ld, int rows, int r0, 
 // tile_base points at element (r0, k0) of the operand; T is the LDS tile
 __device__ __forceinline__ void kmaj_issue(const bf16_t* tile_base, const KmajLoads& L, bf16_t* T,
                                            int w) {
+    const buf_rsrc_t r = make_rsrc(tile_base);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const char* g = reinterpret_cast<const char*>(tile_base) + L.off[i];
-        __builtin_amdgcn_global_load_lds(
-            (const void*)g, (__attribute__((address_space(3))) void*)(T + (i * 8 + w) * 512), 16,
-            0, 0);
-    }
+    for (int i = 0; i < 4; ++i) lds_copy<16>(r, (int)L.off[i], T + (i * 8 + w) * 512);
 }
 
 // mn-major operand P(r, k) = P[k * ld + r]: the tile is stored as it lies in
 // memory, 64 k rows of 256 r (512 bytes, 32 chunks), chunk c of k row kr at
 // chunk position c ^ ((kr & 3) << 2).  Copy instruction i of wave w fills k
 // rows 2 (8 i + w) and 2 (8 i + w) + 1; lane l takes row + (l >> 5), chunk
-// position l & 31.  Chunks past `rows` are redirected to column 0 of the
-// same k row (their products land in outputs that are never stored).
-// Requires k0 + 64 <= K.
+// position l & 31.  Chunks past `rows` get an offset beyond the buffer
+// resource's range, which the copy turns into zeros (their products land in
+// outputs that are never stored).  Requires k0 + 64 <= K.
+constexpr int kOutOfRange = (int)0x80000000u;
 struct MnLoads {
     int off[4];   // byte offsets of this lane's four chunks from element (k0, r0)
 };
@@ -189,21 +186,16 @@ __device__ __forceinline__ MnLoads mn_offsets(int64_t ld, int rows, int r0, int 
     for (int i = 0; i < 4; ++i) {
         const int kr = 2 * (8 * i + w) + (lane >> 5);
         const int c = (lane & 31) ^ ((kr & 3) << 2);
-        const int col = r0 + 8 * c < rows ? 8 * c : -r0;
-        L.off[i] = (int)(((int64_t)kr * ld + col) * 2);
+        L.off[i] = r0 + 8 * c < rows ? (int)(((int64_t)kr * ld + 8 * c) * 2) : kOutOfRange;
     }
     return L;
 }
 
 __device__ __forceinline__ void mn_issue(const bf16_t* tile_base, const MnLoads& L, bf16_t* T,
                                          int w) {
+    const buf_rsrc_t r = make_rsrc(tile_base);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const char* g = reinterpret_cast<const char*>(tile_base) + L.off[i];
-        __builtin_amdgcn_global_load_lds(
-            (const void*)g, (__attribute__((address_space(3))) void*)(T + (i * 8 + w) * 512), 16,
-            0, 0);
-    }
+    for (int i = 0; i < 4; ++i) lds_copy<16>(r, L.off[i], T + (i * 8 + w) * 512);
 }
 
 // byte offset, in an mn-major tile, of this lane's first transpose read for
