@@ -108,19 +108,6 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     return s;
 }
 
-// tanh from its Taylor series near 0 and from 1 - 2/(exp(2x)+1) elsewhere
-__device__ __forceinline__ float tanh_f(float x) {
-    float ax = fabsf(x);
-    if (ax < 0.125f) {
-        float x2 = x * x;
-        // x - x^3/3 + 2x^5/15 - 17x^7/315
-        return x * (1.f + x2 * (-1.f / 3.f + x2 * (2.f / 15.f + x2 * (-17.f / 315.f))));
-    }
-    float e = __expf(2.f * ax);
-    float t = 1.f - 2.f / (e + 1.f);
-    return copysignf(t, x);
-}
-
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------ HBM -> LDS copies

@@ -239,16 +239,26 @@ __device__ __forceinline__ void unpack_chunk<bf16_t>(const uint4& raw, float* ou
     out[4] = bf_lo(raw.z); out[5] = bf_hi(raw.z); out[6] = bf_lo(raw.w); out[7] = bf_hi(raw.w);
 }
 
+// tanh(y) = 1 - 2 / (exp(2y) + 1) on the hardware exp2 and reciprocal units;
+// saturates to +-1 (exp2 overflow gives 1/inf = 0).  Returns r = 1/(exp(2y)+1)
+// so that tanh = 1 - 2r and the softcapped logit is s (1 - 2r).
+__device__ __forceinline__ float tanh_r(float y) {
+    return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y * 2.8853900817779268f) + 1.f);
+}
+
 template <typename T, int MAXC>
 __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     T* __restrict__ z, int64_t ldz, int V, int N, const int32_t* __restrict__ tgt,
     float cap, const float* __restrict__ rowscale, float inv_n,
     float* __restrict__ tok_loss, int want_grad) {
     constexpr int VEC = Elt<T>::kVec;
+    constexpr float kL2e = 1.4426950408889634f;
     __shared__ float red[kCeThreads / 64];
     const int64_t row = blockIdx.x;
     T* zr = z + row * ldz;
     const float inv_cap = 1.f / cap;
+    // exp(c) = 2^(s log2e (1 - 2r)) = 2^(a + b r)
+    const float a = cap * kL2e, bb = -2.f * cap * kL2e;
     uint4 raw[MAXC];
     float ssum = 0.f;
 #pragma unroll
@@ -258,22 +268,29 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
             raw[ci] = *reinterpret_cast<const uint4*>(zr + c);
             float v[VEC];
             unpack_chunk<T>(raw[ci], v);
+            if (c + VEC <= V) {
 #pragma unroll
-            for (int k = 0; k < VEC; ++k)
-                if (c + k < V) ssum += __expf(cap * tanh_f(v[k] * inv_cap));
+                for (int k = 0; k < VEC; ++k)
+                    ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * inv_cap), a));
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    if (c + k < V) ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * inv_cap), a));
+            }
         }
     }
     ssum = block_sum(ssum, red);
     const float lse = __logf(ssum);
     const int y = tgt[row];
     if (threadIdx.x == 0) {
-        const float cy = cap * tanh_f(Elt<T>::ld(zr + y) * inv_cap);
+        const float cy = cap * (1.f - 2.f * tanh_r(Elt<T>::ld(zr + y) * inv_cap));
         tok_loss[row] = lse - cy;
     }
     if (!want_grad) return;
     // every thread has finished reading z[y] before any thread overwrites it
     __syncthreads();
     const float sc = rowscale[row] * inv_n;
+    const float a2 = a - lse * kL2e;   // exp(c - lse) = 2^(a2 + b r)
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int64_t c = ((int64_t)ci * kCeThreads + threadIdx.x) * VEC;
@@ -282,14 +299,23 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
             unpack_chunk<T>(raw[ci], v);
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
-                if (c + k < V) {
-                    const float cv = cap * tanh_f(v[k] * inv_cap);
-                    const float p = __expf(cv - lse) - ((c + k) == y ? 1.f : 0.f);
-                    const float u = cv * inv_cap;
-                    o[k] = sc * p * (1.f - u * u);
-                } else {
-                    o[k] = 0.f;
-                }
+                // dL/dz = (softmax(c) - onehot) (1 - (c/s)^2) = (p - onehot) (1 - t^2)
+                const float r = tanh_r(v[k] * inv_cap);
+                const float t = fmaf(-2.f, r, 1.f);
+                const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));
+                o[k] = sc * p * fmaf(-t, t, 1.f);
+            }
+            if (c + VEC > V)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    if (c + k >= V) o[k] = 0.f;
+            if (y >= c && y < c + VEC) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k)
+                    if (c + k == y) {
+                        const float t = fmaf(-2.f, tanh_r(v[k] * inv_cap), 1.f);
+                        o[k] -= sc * fmaf(-t, t, 1.f);
+                    }
             }
             st_vec<T>(zr + c, o);
         }
