@@ -281,12 +281,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 }
 
 // ------------------------------------------------------------------ backward: dq
-template <int HD>
+template <int HD, bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, int B, int T, int H,
-    float scale_log2, float scale) {
+    float scale_log2, float scale, AttnBwdFuse fz) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
     __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
 
@@ -377,7 +377,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
             }
         }
     }
-    if (valid) {
+    if (!valid) return;
+    if constexpr (!FUSE) {
         float* out = dq + (seq0 * H + r) * HD;
 #pragma unroll
         for (int db = 0; db < HD / 32; ++db)
@@ -387,6 +388,56 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
                 *reinterpret_cast<float4*>(out + d) =
                     make_float4(acc[db][4 * gq] * scale, acc[db][4 * gq + 1] * scale,
                                 acc[db][4 * gq + 2] * scale, acc[db][4 * gq + 3] * scale);
+            }
+    } else {
+        // lane holds dq~ of row (t, j) at d = 32 db + 8 gq + 4 g + e (lane ^ 32
+        // holds the other half of the row): QK-norm backward, then the
+        // transposed rotation pairs d with d + hd/2 (block db + hd/64)
+        const int64_t tok = seq0 + t;
+        const bf16_t* yrow = fz.y + tok * ldq + (int64_t)j * HD;
+        float yv[HD / 32][16];
+        float dot = 0.f;
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const uint2 w2 = *reinterpret_cast<const uint2*>(yrow + 32 * db + 8 * gq + 4 * g);
+                const float yy[4] = {bf_lo(w2.x), bf_hi(w2.x), bf_lo(w2.y), bf_hi(w2.y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[db][4 * gq + e] *= scale;
+                    yv[db][4 * gq + e] = yy[e];
+                    dot += acc[db][4 * gq + e] * yy[e];
+                }
+            }
+        dot += __shfl_xor(dot, 32, 64);
+        const float rr = fz.rqk[tok * (H + 1) + j];
+        const float mean = dot / (float)HD, sc = fz.r1[tok];
+        bf16_t* orow = fz.dqkv + tok * ldq + (int64_t)j * HD;
+        constexpr int HALF = HD / 2, DB2 = HD / 64;
+        const float* ct = fz.cos_t + (int64_t)t * HALF;
+        const float* st = fz.sin_t + (int64_t)t * HALF;
+#pragma unroll
+        for (int db = 0; db < DB2; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d = 32 * db + 8 * gq + 4 * g;
+                const float4 c4 = *reinterpret_cast<const float4*>(ct + d);
+                const float4 s4 = *reinterpret_cast<const float4*>(st + d);
+                const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+                float o0[4], o1[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a0 = rr * (acc[db][4 * gq + e] - yv[db][4 * gq + e] * mean);
+                    const float a1 =
+                        rr * (acc[db + DB2][4 * gq + e] - yv[db + DB2][4 * gq + e] * mean);
+                    o0[e] = sc * (a0 * cs[e] + a1 * sn[e]);
+                    o1[e] = sc * (a1 * cs[e] - a0 * sn[e]);
+                }
+                *reinterpret_cast<uint2*>(orow + d) =
+                    make_uint2(pack_bf2(o0[0], o0[1]), pack_bf2(o0[2], o0[3]));
+                *reinterpret_cast<uint2*>(orow + d + HALF) =
+                    make_uint2(pack_bf2(o1[0], o1[1]), pack_bf2(o1[2], o1[3]));
             }
     }
 }
@@ -591,13 +642,14 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
 
 // dk[b*T + key] = sum over the chunks of the key's block of the partials, in
 // chunk order (same for dv); one thread per 4 consecutive elements
-template <int HD>
+template <int HD, bool FUSE>
 __global__ __launch_bounds__(256) void k_attn_dkv_reduce(const float* __restrict__ dk_part,
                                                          const float* __restrict__ dv_part,
                                                          float* __restrict__ dk,
                                                          float* __restrict__ dv, int B, int T,
                                                          int H, int chunk_rows,
-                                                         int slots_per_seq) {
+                                                         int slots_per_seq, int64_t ld,
+                                                         AttnBwdFuse fz) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (int64_t)B * T * (HD / 4)) return;
     const int d4 = (int)(idx % (HD / 4));
@@ -616,8 +668,41 @@ __global__ __launch_bounds__(256) void k_attn_dkv_reduce(const float* __restrict
         a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
         c.x += y.x; c.y += y.y; c.z += y.z; c.w += y.w;
     }
-    *reinterpret_cast<float4*>(dk + tok * HD + d4 * 4) = a;
-    *reinterpret_cast<float4*>(dv + tok * HD + d4 * 4) = c;
+    if constexpr (!FUSE) {
+        *reinterpret_cast<float4*>(dk + tok * HD + d4 * 4) = a;
+        *reinterpret_cast<float4*>(dv + tok * HD + d4 * 4) = c;
+    } else {
+        // the HD/4 threads of a token are consecutive lanes; element d pairs
+        // with d + hd/2, HD/8 lanes away
+        const int d = d4 * 4;
+        const float sc = fz.r1[tok];
+        const bf16_t* yk = fz.y + tok * ld + (int64_t)H * HD;
+        const uint2 w2 = *reinterpret_cast<const uint2*>(yk + d);
+        const float y[4] = {bf_lo(w2.x), bf_hi(w2.x), bf_lo(w2.y), bf_hi(w2.y)};
+        float gk[4] = {a.x, a.y, a.z, a.w};
+        float dot = gk[0] * y[0] + gk[1] * y[1] + gk[2] * y[2] + gk[3] * y[3];
+        dot = group_sum(dot, HD / 4);
+        const float rr = fz.rqk[tok * (H + 1) + H], mean = dot / (float)HD;
+        float an[4], ap[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) an[e] = rr * (gk[e] - y[e] * mean);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ap[e] = __shfl_xor(an[e], HD / 8, 64);
+        constexpr int HALF = HD / 2;
+        const bool lo = d < HALF;
+        const int i = lo ? d : d - HALF;
+        const float4 c4 = *reinterpret_cast<const float4*>(fz.cos_t + (int64_t)kk * HALF + i);
+        const float4 s4 = *reinterpret_cast<const float4*>(fz.sin_t + (int64_t)kk * HALF + i);
+        const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = lo ? sc * (an[e] * cs[e] + ap[e] * sn[e]) : sc * (an[e] * cs[e] - ap[e] * sn[e]);
+        bf16_t* out = fz.dqkv + tok * ld + (int64_t)H * HD;
+        *reinterpret_cast<uint2*>(out + d) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+        *reinterpret_cast<uint2*>(out + HD + d) =
+            make_uint2(pack_bf2(sc * c.x, sc * c.y), pack_bf2(sc * c.z, sc * c.w));
+    }
 }
 
 int kv_slots_per_seq(int T, int H, int chunk_rows) {
@@ -645,7 +730,8 @@ template <int HD>
 hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                       int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
                       float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
-                      hipStream_t s) {
+                      hipStream_t s, const AttnBwdFuse* fuse) {
+    const AttnBwdFuse fz = fuse ? *fuse : AttnBwdFuse{};
     // scratch: delta [B*T*H], then the dK and dV partials
     float* delta = scratch;
     const int slots = kv_slots_per_seq(T, H, kChunkRows);
@@ -669,8 +755,13 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     e = prof_cut("attn_bwd_dq", 3 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows +
                                                           rows * HD * 4.0);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_bwd_dq_mfma<HD>, dim3(n_rb * B), dim3(256), 0, s, q, k, v, ldq,
-                       ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale);
+    // fused: dq~ goes through QK-norm and rotary backward into bf16 dqkv
+    if (fuse)
+        hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, true>), dim3(n_rb * B), dim3(256), 0, s, q, k,
+                           v, ldq, ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
+    else
+        hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, false>), dim3(n_rb * B), dim3(256), 0, s, q,
+                           k, v, ldq, ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dkv: S, dP, dV and dK; writes one partial per chunk
@@ -685,8 +776,14 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     e = prof_cut("attn_dkv_reduce", 0, part_b + 2.0 * toks * HD * 4.0);
     if (e != hipSuccess) return e;
     const int64_t n4 = (int64_t)B * T * (HD / 4);
-    hipLaunchKernelGGL(k_attn_dkv_reduce<HD>, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s,
-                       dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots);
+    if (fuse)
+        hipLaunchKernelGGL((k_attn_dkv_reduce<HD, true>), dim3((unsigned)ceil_div(n4, 256)),
+                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots,
+                           ldq, fz);
+    else
+        hipLaunchKernelGGL((k_attn_dkv_reduce<HD, false>), dim3((unsigned)ceil_div(n4, 256)),
+                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots,
+                           ldq, fz);
     return hipGetLastError();
 }
 
@@ -703,11 +800,15 @@ hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
                          float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
-                         int hd, hipStream_t s) {
+                         int hd, hipStream_t s, const AttnBwdFuse* fuse) {
+    // the fused tail writes into the qkv layout: q, k, v must be one buffer
+    if (fuse && (k != q + (int64_t)H * hd || v != k + hd || ldkv != ldq)) return hipErrorInvalidValue;
     if (hd == 128)
-        return launch_bwd<128>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s);
+        return launch_bwd<128>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s,
+                               fuse);
     if (hd == 64)
-        return launch_bwd<64>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s);
+        return launch_bwd<64>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, T, H, s,
+                              fuse);
     return hipErrorInvalidValue;
 }
 

@@ -39,7 +39,17 @@ struct EpiDev {
     const float* rowscale;
     const void* aux;
     int accumulate;
+    const float* cos_t;
+    const float* sin_t;
+    float* rqk;
+    int seq_len, n_head, head_dim;
+    float eps;
 };
+
+EpiDev make_epi(const Epilogue& p) {
+    return EpiDev{p.mode,   p.rowscale, p.aux,     p.accumulate ? 1 : 0, p.cos_t, p.sin_t,
+                  p.rqk,    p.seq_len,  p.n_head,  p.head_dim,           p.eps};
+}
 
 template <typename T>
 __device__ __forceinline__ float epi_value(const EpiDev& e, int64_t m, int64_t idx, float acc) {
@@ -283,6 +293,49 @@ __device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, 
     }
 }
 
+// QKV epilogue for 4 consecutive columns n .. n+3 of row m held by lane li of
+// a half-wave whose 32 lanes hold one 128-column stretch of the row (so every
+// head of head_dim <= 128 lies in an aligned group of head_dim/4 lanes).
+// u = rowscale * acc; a query or key head is rotated -- element i < hd/2 pairs
+// with i + hd/2, which sits hd/8 lanes away -- and RMS-normalised over its
+// group; the value head is stored as u.
+__device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
+                                               int N, int64_t m, int64_t n, int li, float4 v) {
+    const int hd = e.head_dim, half = hd >> 1, H = e.n_head;
+    const bool valid = m < M && n < N;
+    const float rs = valid ? e.rowscale[m] : 0.f;
+    float x[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
+    const int head = (int)(n / hd);              // uniform over the lane group
+    const int d = (int)(n - (int64_t)head * hd); // first of this lane's 4 elements
+    if (head <= H) {
+        const int lanes = hd >> 2;               // lanes per head
+        float px[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) px[q] = __shfl_xor(x[q], lanes >> 1, 64);
+        const int i = d < half ? d : d - half;
+        const int64_t pos = valid ? m % e.seq_len : 0;
+        const float4 c4 = *reinterpret_cast<const float4*>(e.cos_t + pos * half + i);
+        const float4 s4 = *reinterpret_cast<const float4*>(e.sin_t + pos * half + i);
+        const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // first half: x0 = own, x1 = partner; second half: x0 = partner, x1 = own
+            const float y = d < half ? x[q] * cs[q] - px[q] * sn[q] : px[q] * sn[q] + x[q] * cs[q];
+            x[q] = y;
+            ss += y * y;
+        }
+        ss = group_sum(ss, lanes);
+        const float rr = 1.f / sqrtf(ss / (float)hd + e.eps);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] *= rr;
+        if (valid && d == 0) e.rqk[m * (H + 1) + head] = rr;
+    }
+    if (valid)
+        *reinterpret_cast<uint2*>(C + m * ldc + n) =
+            make_uint2(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]));
+}
+
 // 512 threads: wave w owns m rows wm*64 .. +63 (wm = w & 3) and n rows
 // wn*128 .. +127 (wn = w >> 2) of the 256 x 256 tile: 2 x 4 accumulator blocks.
 // In a k-major tile, fragment row 32 i + (lane & 31) of a 32-aligned block
@@ -444,6 +497,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             const int row = 2 * t + hi;
             const float4 v = *reinterpret_cast<const float4*>(stage + row * 128 + ((li ^ row) << 2));
             const int64_t m = m0 + wm * 64 + 32 * j + row;
+            if (MODE == EPI_QKV_ROPE) {
+                // every lane of the half-wave joins the head's shuffles
+                qkv_rope_store(e, static_cast<bf16_t*>(C), ldc, M, N, m, n, li, v);
+                continue;
+            }
             if (m >= M) continue;
             if (full_n || n + 3 < N) {
                 epi_vec4<MODE>(e, C, m * ldc + n, m, v.x, v.y, v.z, v.w);
@@ -515,7 +573,8 @@ hipError_t gemm<float>(int M, int N, int K, const float* A, int64_t lda, bool a_
                        const float* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
                        const Epilogue& epi, float*, size_t, hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    EpiDev e{epi.mode, epi.rowscale, epi.aux, epi.accumulate ? 1 : 0};
+    if (epi.mode == EPI_QKV_ROPE) return hipErrorInvalidValue;   // bf16 only
+    const EpiDev e = make_epi(epi);
     dim3 grid((unsigned)ceil_div(N, kSB), (unsigned)ceil_div(M, kSB));
     hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, s, M, N, K, A, lda,
                        a_kmajor ? 1 : 0, B, ldb, b_kmajor ? 1 : 0, C, ldc, e);
@@ -528,7 +587,11 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
                         const Epilogue& epi, float* splitk_ws, size_t splitk_ws_bytes,
                         hipStream_t s) {
     if (M <= 0 || N <= 0) return hipSuccess;
-    EpiDev e{epi.mode, epi.rowscale, epi.aux, epi.accumulate ? 1 : 0};
+    const EpiDev e = make_epi(epi);
+    if (epi.mode == EPI_QKV_ROPE &&
+        (epi.head_dim <= 0 || 128 % epi.head_dim || epi.head_dim % 8 || !epi.cos_t ||
+         !epi.sin_t || !epi.rqk || epi.seq_len <= 0 || N != (epi.n_head + 2) * epi.head_dim))
+        return hipErrorInvalidValue;
     int splits = 1;
     if (epi.mode == EPI_STORE_F32) {
         splits = choose_splits(M, N, K);
@@ -565,6 +628,9 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
                 break;
             case EPI_STORE_T:
                 err = launch_mfma<true, true, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                break;
+            case EPI_QKV_ROPE:
+                err = launch_mfma<true, true, EPI_QKV_ROPE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
                 break;
             default: return hipErrorInvalidValue;
         }

@@ -22,12 +22,23 @@ enum EpiMode : int {
     EPI_RESID = 3,       // C[m][n] = resid[m][n] + acc   (resid: T, ld = ldc)
     EPI_RELU2_BWD = 4,   // C[m][n] = rowscale[m] * acc * 2*sqrt(aux[m][n]) (aux: T, ld = ldc)
     EPI_STORE_T = 5,     // C[m][n] = acc, stored as T
+    // QKV projection: u = rowscale[m] * acc; the query heads and the key head
+    // of row m (position m % seq_len) are rotated and RMS-normalised, rqk
+    // receives each head's 1/rms; the value head is stored as u.  bf16 only;
+    // head_dim must divide 128.
+    EPI_QKV_ROPE = 6,
 };
 struct Epilogue {
     int mode = EPI_STORE_F32;
     const float* rowscale = nullptr;
     const void* aux = nullptr;   // resid or g, element type T, same ld as C
     bool accumulate = false;     // EPI_STORE_F32 only
+    // EPI_QKV_ROPE
+    const float* cos_t = nullptr;   // [seq_len, head_dim / 2]
+    const float* sin_t = nullptr;
+    float* rqk = nullptr;           // [M, n_head + 1]
+    int seq_len = 0, n_head = 0, head_dim = 0;
+    float eps = 0.f;
 };
 
 template <typename T>
@@ -54,10 +65,25 @@ hipError_t attn_delta(const T* o, const T* dout, int64_t rows, int hd, float* de
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,
                          hipStream_t s);
+// Tail of the step's attention backward fused into the bf16 kernels: instead
+// of fp32 dq, dk, dv they write dqkv (bf16, same layout and stride as qkv) =
+// r1[token] times, for the query heads and the key head, the backward of
+// QK-norm then rotary (y: the saved normalised, rotated qkv; rqk: each head's
+// 1/rms; cos_t, sin_t: [T, hd/2] tables), and r1[token] * dv for the value
+// head.
+struct AttnBwdFuse {
+    const bf16_t* y = nullptr;
+    const float* rqk = nullptr;
+    const float* r1 = nullptr;
+    const float* cos_t = nullptr;
+    const float* sin_t = nullptr;
+    bf16_t* dqkv = nullptr;
+};
+// fuse == nullptr: plain fp32 dq, dk, dv outputs
 hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
                          float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
-                         int hd, hipStream_t s);
+                         int hd, hipStream_t s, const AttnBwdFuse* fuse = nullptr);
 // bytes of the scratch attn_bwd needs (row sums of dO*O and dK/dV partials)
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 // Causal multi-query attention of B sequences of length T with H query heads

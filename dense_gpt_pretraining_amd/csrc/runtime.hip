@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/nc.h"
@@ -307,12 +308,27 @@ struct Step {
             T* qkv = QKV(sl);
             NC_RUN("rms_stats", 0, rowb + N * 4.0,
                    nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
-            NC_RUN("gemm_nt_rowscale", gf(N, Wq, D), gb(N, Wq, D, es(), N * 4.0),
-                   nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
-                               Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
-            NC_RUN("rope_qknorm_fwd", 0, 2.0 * N * (H + 1) * hd * es() + N * (H + 1) * 4.0,
-                   nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t, sin_t,
-                                          eps, RQK(sl), s));
+            if constexpr (std::is_same<T, nc::bf16_t>::value) {
+                // rotary + QK-norm in the projection's epilogue
+                nc::Epilogue e = epi(nc::EPI_QKV_ROPE, r1);
+                e.cos_t = cos_t;
+                e.sin_t = sin_t;
+                e.rqk = RQK(sl);
+                e.seq_len = c.seq_len;
+                e.n_head = (int)H;
+                e.head_dim = (int)hd;
+                e.eps = eps;
+                NC_RUN("gemm_nt_qkv_rope", gf(N, Wq, D), gb(N, Wq, D, es(), N * (H + 5.0) * 4.0),
+                       nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true,
+                                   qkv, Wq, e, nullptr, 0, s));
+            } else {
+                NC_RUN("gemm_nt_rowscale", gf(N, Wq, D), gb(N, Wq, D, es(), N * 4.0),
+                       nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true,
+                                   qkv, Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
+                NC_RUN("rope_qknorm_fwd", 0, 2.0 * N * (H + 1) * hd * es() + N * (H + 1) * 4.0,
+                       nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t,
+                                              sin_t, eps, RQK(sl), s));
+            }
             NC_RUN("attn_fwd", 4.0 * hd * H * pairs(),
                    2.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 4.0,
                    nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
@@ -416,17 +432,38 @@ struct Step {
                                false, G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb,
                                s));
             T* qkv = QKV(l);
-            NC_RUN("attn_bwd", 8.0 * hd * H * pairs(),
-                   4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
-                       4.0 * N * (H + 2) * hd,
-                   nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
-                                   LSE(l), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
-                                   (int)H, (int)hd, s));
-            NC_RUN("rope_qknorm_bwd", 0,
-                   N * (H + 1) * hd * es() + 4.0 * N * (H + 2) * hd + N * (H + 2) * hd * es() +
-                       N * (H + 2) * 4.0,
-                   nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
-                                          (int)H, (int)hd, cos_t, sin_t, dqkv, s));
+            if constexpr (std::is_same<T, nc::bf16_t>::value) {
+                // QK-norm and rotary backward fused into the attention kernels,
+                // which write the bf16 dqkv directly
+                nc::AttnBwdFuse fz;
+                fz.y = reinterpret_cast<const nc::bf16_t*>(qkv);
+                fz.rqk = RQK(l);
+                fz.r1 = R1(l);
+                fz.cos_t = cos_t;
+                fz.sin_t = sin_t;
+                fz.dqkv = reinterpret_cast<nc::bf16_t*>(dqkv);
+                const nc::bf16_t* qb = reinterpret_cast<const nc::bf16_t*>(qkv);
+                NC_RUN("attn_bwd", 8.0 * hd * H * pairs(),
+                       4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
+                           N * (H + 2) * hd * es(),
+                       nc::attn_bwd_mfma(qb, qb + H * hd, qb + (H + 1) * hd, Wq, Wq,
+                                         reinterpret_cast<const nc::bf16_t*>(O(l)),
+                                         reinterpret_cast<const nc::bf16_t*>(dout), LSE(l),
+                                         at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
+                                         (int)H, (int)hd, s, &fz));
+            } else {
+                NC_RUN("attn_bwd", 8.0 * hd * H * pairs(),
+                       4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
+                           4.0 * N * (H + 2) * hd,
+                       nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
+                                       LSE(l), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
+                                       (int)H, (int)hd, s));
+                NC_RUN("rope_qknorm_bwd", 0,
+                       N * (H + 1) * hd * es() + 4.0 * N * (H + 2) * hd + N * (H + 2) * hd * es() +
+                           N * (H + 2) * 4.0,
+                       nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
+                                              (int)H, (int)hd, cos_t, sin_t, dqkv, s));
+            }
             NC_RUN("transpose_w", 0, tb(Wq, D),
                    nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
             NC_RUN("gemm_nt_f32", gf(N, D, Wq), gb(N, D, Wq, 4.0),
