@@ -293,6 +293,30 @@ __device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, 
     }
 }
 
+// epi_vec4 with the row scale and the 4 aux values already in registers
+template <int MODE>
+__device__ __forceinline__ void epi_vec4_pre(const EpiDev& e, void* C, int64_t idx, float4 v,
+                                             uint2 a, float rs) {
+    if (MODE == EPI_STORE_F32) {
+        epi_vec4<MODE>(e, C, idx, 0, v.x, v.y, v.z, v.w);
+        return;
+    }
+    float o[4] = {v.x, v.y, v.z, v.w};
+    const float x[4] = {bf_lo(a.x), bf_hi(a.x), bf_lo(a.y), bf_hi(a.y)};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (MODE == EPI_RESID) o[q] += x[q];
+        if (MODE == EPI_RELU2_BWD) o[q] *= 2.f * rs * __builtin_amdgcn_sqrtf(x[q]);
+        if (MODE == EPI_ROWSCALE) o[q] *= rs;
+        if (MODE == EPI_ROWSCALE_RELU2) {
+            const float u = fmaxf(rs * o[q], 0.f);
+            o[q] = u * u;
+        }
+    }
+    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(C) + idx) =
+        make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+}
+
 // QKV epilogue for 4 consecutive columns n .. n+3 of row m held by lane li of
 // a half-wave whose 32 lanes hold one 128-column stretch of the row (so every
 // head of head_dim <= 128 lies in an aligned group of head_dim/4 lanes).
@@ -479,8 +503,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     float* stage = reinterpret_cast<float*>(wave < 4 ? lds0 : lds1) + (wave & 3) * 4096;
     const bool full_n = n0 + kTN <= N;
     const int li = lane & 31, hi = lane >> 5;
+    constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
+    constexpr bool kRs = MODE == EPI_ROWSCALE || MODE == EPI_ROWSCALE_RELU2 || MODE == EPI_RELU2_BWD;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
+        // the pass's epilogue inputs are requested before the LDS round trip
+        uint2 auxv[16];
+        float rsv[16];
+        {
+            const int64_t n = n0 + wn * 128 + 4 * li;
+            const bool nok = full_n || n + 3 < N;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
+                auxv[t] = make_uint2(0, 0);
+                rsv[t] = 0.f;
+                if (kAux && m < M && nok)
+                    auxv[t] = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(e.aux) +
+                                                              m * ldc + n);
+                if (kRs && m < M) rsv[t] = e.rowscale[m];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -492,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             }
         __syncthreads();
         const int64_t n = n0 + wn * 128 + 4 * li;
-#pragma unroll 4
+#pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int row = 2 * t + hi;
             const float4 v = *reinterpret_cast<const float4*>(stage + row * 128 + ((li ^ row) << 2));
@@ -504,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             }
             if (m >= M) continue;
             if (full_n || n + 3 < N) {
-                epi_vec4<MODE>(e, C, m * ldc + n, m, v.x, v.y, v.z, v.w);
+                epi_vec4_pre<MODE>(e, C, m * ldc + n, v, auxv[t], rsv[t]);
             } else {
                 const float a[4] = {v.x, v.y, v.z, v.w};
                 for (int q = 0; q < 4; ++q)
