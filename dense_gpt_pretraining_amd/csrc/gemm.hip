@@ -480,13 +480,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             for (int ks = 0; ks < kTK / 16; ++ks) {
                 const int cs = ks & 1;
                 if (ks + 1 < kTK / 16) rd(cur, ks + 1, cs ^ 1);
-                // keep the next step's reads ahead of this step's products
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
+                // interleave the next step's fragment reads with this step's
+                // products: MFMA, read, MFMA, read, ...
+                if (ks + 1 < kTK / 16) {
+#pragma unroll
+                    for (int x = 0; x < (AK && BK ? 6 : 12); ++x) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);       // the rest
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
