@@ -33,7 +33,8 @@
 // the rescale is rare -- exact, because O and l always share the same stale
 // max.  Output O and the log-sum-exp per row.
 // Backward: dQ by a row-block kernel that recomputes P from the saved
-// log-sum-exp; dK, dV by a key-block kernel that streams the query rows that
+// log-sum-exp (and first forms delta = rowsum(dO * O) of its rows, which the
+// next kernel reads); dK, dV by a key-block kernel that streams the query rows that
 // can see its keys, cut into chunks whose partial sums are added in chunk
 // order.  No atomics: the result is deterministic.
 #include "kernels.h"
@@ -284,9 +285,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 template <int HD, bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dq, int B, int T, int H,
-    float scale_log2, float scale, AttnBwdFuse fz) {
+    int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq, int B,
+    int T, int H, float scale_log2, float scale, AttnBwdFuse fz) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
     __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
 
@@ -317,7 +318,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     }
     // p = 2^(s * scale_log2 - lse_row * log2 e)
     const float nl2 = valid ? -lse[seq0 * H + r] * kLog2e : 0.f;
-    const float dl = valid ? delta[seq0 * H + r] : 0.f;
+    // delta = rowsum(dO * O): this lane holds half of the row's dO (the k
+    // steps' 8g.. elements), lane ^ 32 the other half; the dK/dV kernel reads
+    // the value back
+    float dl = 0.f;
+    if (valid) {
+        const bf16_t* orow = o + (seq0 * H + r) * HD;
+#pragma unroll
+        for (int kk = 0; kk < HD / 16; ++kk) {
+            const uint4 ov = *reinterpret_cast<const uint4*>(orow + 16 * kk + 8 * g);
+            const uint4 dv4 = __builtin_bit_cast(uint4, df[kk]);
+            dl += bf_lo(ov.x) * bf_lo(dv4.x) + bf_hi(ov.x) * bf_hi(dv4.x) +
+                  bf_lo(ov.y) * bf_lo(dv4.y) + bf_hi(ov.y) * bf_hi(dv4.y) +
+                  bf_lo(ov.z) * bf_lo(dv4.z) + bf_hi(ov.z) * bf_hi(dv4.z) +
+                  bf_lo(ov.w) * bf_lo(dv4.w) + bf_hi(ov.w) * bf_hi(dv4.w);
+        }
+    }
+    dl += __shfl_xor(dl, 32, 64);
+    if (valid && g == 0) delta[seq0 * H + r] = dl;
     const int last_row = min(r0 + kRB - 1, rows_total - 1);
     const int n_tiles = (last_row / H) / kKT + 1;
     const int w_first = r0 + 32 * w;
@@ -744,24 +762,22 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const double rows = (double)B * T * H, toks = (double)B * T;
     const double pairs = (double)B * H * T * (T + 1) / 2.0;
     const double qo_b = rows * HD * 2.0, kv_b = toks * HD * 2.0;
-    hipError_t e = prof_label("attn_delta", 0, 2 * qo_b + rows * 4.0);
-    if (e != hipSuccess) return e;
-    e = attn_delta<bf16_t>(o, dout, (int64_t)B * T * H, HD, delta, s);
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const float scale = 1.f / sqrtf((float)HD);
     const float scale_log2 = kLog2e * scale;
     const int n_rb = (T * H + kRB - 1) / kRB;
-    // dq: S, dP and dQ
-    e = prof_cut("attn_bwd_dq", 3 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows +
-                                                          rows * HD * 4.0);
+    // dq: delta = rowsum(dO * O), then S, dP and dQ
+    e = prof_label("attn_bwd_dq", 3 * 2.0 * HD * pairs, 3 * qo_b + 2 * kv_b + 8.0 * rows +
+                                                            rows * HD * 4.0);
     if (e != hipSuccess) return e;
     // fused: dq~ goes through QK-norm and rotary backward into bf16 dqkv
     if (fuse)
         hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, true>), dim3(n_rb * B), dim3(256), 0, s, q, k,
-                           v, ldq, ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
+                           v, ldq, ldkv, o, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
     else
         hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, false>), dim3(n_rb * B), dim3(256), 0, s, q,
-                           k, v, ldq, ldkv, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
+                           k, v, ldq, ldkv, o, dout, lse, delta, dq, B, T, H, scale_log2, scale,
+                           fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dkv: S, dP, dV and dK; writes one partial per chunk
