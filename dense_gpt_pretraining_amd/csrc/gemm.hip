@@ -325,19 +325,23 @@ __device__ __forceinline__ void epi_vec4_pre(const EpiDev& e, void* C, int64_t i
 // group; the value head is stored as u.
 __device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
                                                int N, int64_t m, int64_t n, int li, float4 v) {
+    // 32-bit index arithmetic (rows < 2^24, columns < 2^16); head_dim is a
+    // power of two
     const int hd = e.head_dim, half = hd >> 1, H = e.n_head;
-    const bool valid = m < M && n < N;
-    const float rs = valid ? e.rowscale[m] : 0.f;
+    const int hd_shift = __builtin_ctz((unsigned)hd);
+    const int mi = (int)m, ni = (int)n;
+    const bool valid = mi < M && ni < N;
+    const float rs = valid ? e.rowscale[mi] : 0.f;
     float x[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
-    const int head = (int)(n / hd);              // uniform over the lane group
-    const int d = (int)(n - (int64_t)head * hd); // first of this lane's 4 elements
+    const int head = ni >> hd_shift;             // uniform over the lane group
+    const int d = ni & (hd - 1);                 // first of this lane's 4 elements
     if (head <= H) {
         const int lanes = hd >> 2;               // lanes per head
         float px[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) px[q] = __shfl_xor(x[q], lanes >> 1, 64);
         const int i = d < half ? d : d - half;
-        const int64_t pos = valid ? m % e.seq_len : 0;
+        const int pos = valid ? mi % e.seq_len : 0;
         const float4 c4 = *reinterpret_cast<const float4*>(e.cos_t + pos * half + i);
         const float4 s4 = *reinterpret_cast<const float4*>(e.sin_t + pos * half + i);
         const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
@@ -350,10 +354,10 @@ __device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64
             ss += y * y;
         }
         ss = group_sum(ss, lanes);
-        const float rr = 1.f / sqrtf(ss / (float)hd + e.eps);
+        const float rr = __builtin_amdgcn_rsqf(ss / (float)hd + e.eps);
 #pragma unroll
         for (int q = 0; q < 4; ++q) x[q] *= rr;
-        if (valid && d == 0) e.rqk[m * (H + 1) + head] = rr;
+        if (valid && d == 0) e.rqk[(int64_t)mi * (H + 1) + head] = rr;
     }
     if (valid)
         *reinterpret_cast<uint2*>(C + m * ldc + n) =
