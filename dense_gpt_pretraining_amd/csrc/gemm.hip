@@ -445,6 +445,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, buf + kTileElems, wave);
         else mn_issue(B + (int64_t)k0 * ldb + n0, mb, buf + kTileElems, wave);
     };
+    // epilogue aux rows of the first 32-row pass (g of the relu^2 backward),
+    // requested during the last k tile so that their latency hides behind its
+    // products
+    constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
+    const int li = lane & 31, hi = lane >> 5;
+    const bool full_n = n0 + kTN <= N;
+    uint2 aux0[16];
+    auto load_aux = [&](int j, uint2 (&dst)[16]) {
+        const int64_t n = n0 + wn * 128 + 4 * li;
+        const bool nok = full_n || n + 3 < N;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
+            dst[t] = make_uint2(0, 0);
+            if (m < M && nok)
+                dst[t] = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(e.aux) +
+                                                         m * ldc + n);
+        }
+    };
+    // (the residual epilogue keeps its registers for the main loop instead)
+    constexpr bool kPre = MODE == EPI_RELU2_BWD;
+    if (kPre && nk == 0) load_aux(0, aux0);
     if (nk > 0) {
         issue(0, lds0);
         wait_vmem();
@@ -479,6 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                 barrier_nofence();
             }
             if (kt + 1 < nk) issue(kt + 1, nxt);
+            else if (kPre) load_aux(0, aux0);
             rd(cur, 0, 0);
 #pragma unroll
             for (int ks = 0; ks < kTK / 16; ++ks) {
@@ -513,28 +536,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     // 4 (l & 31) .. +3, so 32 lanes cover one row's 128 columns contiguously.
     __syncthreads();   // every wave is done with the last k tile
     float* stage = reinterpret_cast<float*>(wave < 4 ? lds0 : lds1) + (wave & 3) * 4096;
-    const bool full_n = n0 + kTN <= N;
-    const int li = lane & 31, hi = lane >> 5;
-    constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
     constexpr bool kRs = MODE == EPI_ROWSCALE || MODE == EPI_ROWSCALE_RELU2 || MODE == EPI_RELU2_BWD;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         // the pass's epilogue inputs are requested before the LDS round trip
+        // (the first pass's aux rows already are)
         uint2 auxv[16];
         float rsv[16];
-        {
-            const int64_t n = n0 + wn * 128 + 4 * li;
-            const bool nok = full_n || n + 3 < N;
+        if (kAux) {
+            if (kPre && j == 0) {
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
-                auxv[t] = make_uint2(0, 0);
-                rsv[t] = 0.f;
-                if (kAux && m < M && nok)
-                    auxv[t] = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(e.aux) +
-                                                              m * ldc + n);
-                if (kRs && m < M) rsv[t] = e.rowscale[m];
+                for (int t = 0; t < 16; ++t) auxv[t] = aux0[t];
+            } else {
+                load_aux(j, auxv);
             }
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
+            rsv[t] = (kRs && m < M) ? e.rowscale[m] : 0.f;
+            if (!kAux) auxv[t] = make_uint2(0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
