@@ -474,16 +474,18 @@ __host__ __device__ __forceinline__ int kv_chunks(int kb, int H, int rows_total,
 }
 
 template <int HD>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dk_part, float* __restrict__ dv_part,
     int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq) {
     constexpr int TQ = kQT * HD * 2;              // bytes of a Q (or dO) row tile
     constexpr int RPI = 1024 / (HD * 2);          // tile rows per copy instruction
-    constexpr int NI = TQ / 1024 / 4;             // copy instructions per wave per tile
+    constexpr int NI = TQ / 1024 / 8;             // copy instructions per wave per tile
     constexpr int BUF = 2 * TQ + 2 * kQT * 4;     // Q | dO | lse | delta
-    __shared__ __align__(1024) char sm[2 * BUF];
+    // two tile buffers, then the block's V rows (kKB x HD)
+    __shared__ __align__(1024) char sm[2 * BUF + kKB * HD * 2];
+    char* sV = sm + 2 * BUF;
 
     const int rows_total = T * H;
     const int n_kb = (T + kKB - 1) / kKB;
@@ -501,20 +503,35 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
     const int64_t seq0 = (int64_t)b * T;
     const int key0 = kbi * kKB;
     const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    // 8 waves, two per SIMD: wave w owns keys 32 (w & 3) .. +31 of the block and
+    // the row half rh = w >> 2 of every 64-row tile; the two halves' sums are
+    // added (in a fixed order) at the end
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wkey0 = key0 + 32 * w;
+    const int wk = w & 3, rh = w >> 2;
+    const int wkey0 = key0 + 32 * wk;
     const bool wvalid = wkey0 < T;
     const int key = wkey0 + li;
 
-    bf16x8_t kf[HD / 16], vf[HD / 16];
+    // K fragments of the wave's keys stay in registers; the block's V rows go
+    // to LDS (natural layout, chunk swizzle as the tiles), read per k step.
+    // Rows past the sequence end read zeros through the resource's range.
+    bf16x8_t kf[HD / 16];
 #pragma unroll
-    for (int kk = 0; kk < HD / 16; ++kk) {
+    for (int kk = 0; kk < HD / 16; ++kk)
         kf[kk] = wvalid ? as_bf16x8(*reinterpret_cast<const uint4*>(
                               k + (seq0 + key) * ldkv + 16 * kk + 8 * g))
                         : as_bf16x8(make_uint4(0, 0, 0, 0));
-        vf[kk] = wvalid ? as_bf16x8(*reinterpret_cast<const uint4*>(
-                              v + (seq0 + key) * ldkv + 16 * kk + 8 * g))
-                        : as_bf16x8(make_uint4(0, 0, 0, 0));
+    {
+        constexpr int VI = kKB * HD * 2 / 1024 / 8;   // copies per wave
+        const buf_rsrc_t rv = make_rsrc(v + (seq0 + key0) * ldkv,
+                                        (int)((int64_t)(T - key0) * ldkv * 2));
+#pragma unroll
+        for (int i = 0; i < VI; ++i) {
+            const int row = (w * VI + i) * RPI + lane / (HD / 8);
+            const int p = lane % (HD / 8);
+            lds_copy<16>(rv, (int)(row * ldkv * 2) + ((p ^ swz<HD>(row)) << 4),
+                         sV + (w * VI + i) * 1024);
+        }
     }
     f32x16_t dka[HD / 32], dva[HD / 32];
 #pragma unroll
@@ -565,18 +582,24 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
         else if (w == 1)
             lds_copy<4>(make_rsrc(eg + R0), lane * 4, sD + TQ + kQT * 4);
     };
-    int row_off[HD / 16], tr_off[HD / 32][2];
+    // fragment offsets, formed on the fly from a few per-lane values (the
+    // chunk swizzle is an XOR, and the k step / column block only flips bits
+    // the lane part leaves clear): row read of k step kk at
+    // rbase + ((2 kk ^ rx) << 4); transpose read x of column block db at
+    // tbase[x] + ((4 db ^ tx[x]) << 4)
+    const int rbase = li * HD * 2, rx = g ^ swz<HD>(li);
+    int tbase[2], tx[2];
     {
-        const int s = lane & 15, half = (lane >> 4) & 1;
+        const int s4 = lane & 15, half = (lane >> 4) & 1;
 #pragma unroll
-        for (int kk = 0; kk < HD / 16; ++kk) row_off[kk] = toff<HD>(li, 16 * kk + 8 * g);
-#pragma unroll
-        for (int db = 0; db < HD / 32; ++db)
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                tr_off[db][x] = toff<HD>(4 * g + 8 * x + (s >> 2),
-                                         32 * db + 16 * half + 4 * (s & 3));
+        for (int x = 0; x < 2; ++x) {
+            const int row = 4 * g + 8 * x + (s4 >> 2);
+            tbase[x] = row * HD * 2 + (s4 & 1) * 8;
+            tx[x] = (2 * half + ((s4 & 3) >> 1)) ^ swz<HD>(row);
+        }
     }
+    auto row_off = [&](int kk) { return rbase + (((2 * kk) ^ rx) << 4); };
+    auto tr_off = [&](int db, int x) { return tbase[x] + (((4 * db) ^ tx[x]) << 4); };
 
     const int n_qt = (r_end - r_begin) / kQT;
     const int first_vis = key * H;            // first row that sees this lane's key
@@ -592,55 +615,89 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv_mfma(
         const char* sD = sQ + TQ;
         const float* sL = reinterpret_cast<const float*>(sD + TQ);
         if (!wvalid) continue;
-#pragma unroll
-        for (int qb = 0; qb < kQT / 32; ++qb) {
+        {
+            const int qb = rh;
             const int rb0 = R0 + 32 * qb;
             if (rb0 + 31 < w_first_vis) continue;       // no row of the block sees a key
             const char* qr = sQ + qb * 32 * HD * 2;
             const char* dr = sD + qb * 32 * HD * 2;
+            const char* vr = sV + wk * 32 * HD * 2;
             f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
-                s = mfma32(lds_b128(qr + row_off[kk]), kf[kk], s);
-                dp = mfma32(lds_b128(dr + row_off[kk]), vf[kk], dp);
+                s = mfma32(lds_b128(qr + row_off(kk)), kf[kk], s);
+                dp = mfma32(lds_b128(dr + row_off(kk)), lds_b128(vr + row_off(kk)), dp);
             }
-            // lane holds key `key`; register rr holds row rb0 + 8(rr/4) + 4g + rr%4
+            // lane holds key `key`; register rr holds row rb0 + 8(rr/4) + 4g + rr%4.
+            // P and dS are formed one 16-row half (registers 8h .. 8h+7) at a time.
             const bool partial = rb0 < w_all_vis;
-            float p[16], ds[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int ro = 32 * qb + 8 * m + 4 * g;
-                const float4 l4 = *reinterpret_cast<const float4*>(sL + ro);
-                const float4 d4 = *reinterpret_cast<const float4*>(sL + kQT + ro);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rr = 4 * m + e;
-                    float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
-                    if (partial) pv = (rb0 + 8 * m + 4 * g + e >= first_vis) ? pv : 0.f;
-                    p[rr] = pv;
-                    ds[rr] = pv * (dp[rr] - dv4[e]);
-                }
-            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const bf16x8_t bp = pack8(&p[8 * h]);
-                const bf16x8_t bd = pack8(&ds[8 * h]);
+                float p[8], ds[8];
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int m = 2 * h + mm;
+                    const int ro = 32 * qb + 8 * m + 4 * g;
+                    const float4 l4 = *reinterpret_cast<const float4*>(sL + ro);
+                    const float4 d4 = *reinterpret_cast<const float4*>(sL + kQT + ro);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                    const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int rr = 4 * m + e;
+                        float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
+                        if (partial) pv = (rb0 + 8 * m + 4 * g + e >= first_vis) ? pv : 0.f;
+                        p[4 * mm + e] = pv;
+                        ds[4 * mm + e] = pv * (dp[rr] - dv4[e]);
+                    }
+                }
+                const bf16x8_t bp = pack8(p);
+                const bf16x8_t bd = pack8(ds);
                 const char* dt = dr + 16 * h * HD * 2;
                 const char* qt = qr + 16 * h * HD * 2;
 #pragma unroll
                 for (int db = 0; db < HD / 32; ++db) {
-                    dva[db] = mfma32(lds_tr_frag(dt + tr_off[db][0], dt + tr_off[db][1]), bp,
+                    dva[db] = mfma32(lds_tr_frag(dt + tr_off(db, 0), dt + tr_off(db, 1)), bp,
                                      dva[db]);
-                    dka[db] = mfma32(lds_tr_frag(qt + tr_off[db][0], qt + tr_off[db][1]), bd,
+                    dka[db] = mfma32(lds_tr_frag(qt + tr_off(db, 0), qt + tr_off(db, 1)), bd,
                                      dka[db]);
                 }
             }
         }
     }
-    if (wvalid) {
-        const int64_t pslot = ((int64_t)b * slots_per_seq + slot) * kKB + 32 * w + li;
+    // row half 1 hands its sums to row half 0 through LDS (register r of lane
+    // l at float r * 64 + l of the wave's 16 KB slot), dK then dV
+    static_assert(4 * 64 * (HD / 2) * 4 <= 2 * BUF, "exchange fits the tile buffers");
+    float* xch = reinterpret_cast<float*>(sm) + wk * 64 * (HD / 2);
+    wait_vmem();       // no copy is left in flight (a chunk without row tiles)
+    __syncthreads();   // every wave is done with the tile buffers
+    if (rh == 1) {
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = dka[db][r];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dka[db][r] += xch[(db * 16 + r) * 64 + lane];
+    }
+    __syncthreads();
+    if (rh == 1) {
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xch[(db * 16 + r) * 64 + lane] = dva[db][r];
+    }
+    __syncthreads();
+    if (rh == 0 && wvalid) {
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dva[db][r] += xch[(db * 16 + r) * 64 + lane];
+        const int64_t pslot = ((int64_t)b * slots_per_seq + slot) * kKB + 32 * wk + li;
         float* okr = dk_part + pslot * HD;
         float* ovr = dv_part + pslot * HD;
 #pragma unroll
@@ -784,7 +841,7 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const double part_b = 2.0 * B * slots * kKB * HD * 4.0;
     e = prof_cut("attn_bwd_dkv", 4 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows + part_b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(256), 0, s, q, k, v, ldq,
+    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(512), 0, s, q, k, v, ldq,
                        ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2, scale,
                        kChunkRows, slots);
     e = hipGetLastError();

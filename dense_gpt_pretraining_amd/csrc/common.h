@@ -120,6 +120,11 @@ __device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
                                              0x00020000);
 }
+// the same over [base, base + bytes): copies from beyond it read zeros
+__device__ __forceinline__ buf_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                             0x00020000);
+}
 // lane l copies `bytes` (4 or 16) from base + voff to LDS at lds + l * bytes;
 // `lds` must be the same for every lane of the wave
 template <int BYTES>
