@@ -477,19 +477,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         // read while the 8 matrix instructions of step ks issue
         const int rowoff = (lane & 31) * kTK;
         bf16x8_t fa[2][4], fb[2][2];
+        auto rd_a = [&](const bf16_t* sB, int ks, int set, int i) {
+            fa[set][i] = BK ? as_bf16x8(*reinterpret_cast<const uint4*>(
+                                  sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]))
+                            : mn_frag(reinterpret_cast<const char*>(sB) + trb[i] + ks * 16 * 512);
+        };
+        auto rd_b = [&](const bf16_t* sA, int ks, int set, int j) {
+            fb[set][j] = AK ? as_bf16x8(*reinterpret_cast<const uint4*>(
+                                  sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]))
+                            : mn_frag(reinterpret_cast<const char*>(sA) + tra[j] + ks * 16 * 512);
+        };
+        // a step's fragments are read in the order its products first use
+        // them (block i outer, j inner), so its first products wait for the
+        // first two reads only
         auto rd = [&](const bf16_t* buf, int ks, int set) {
             const bf16_t* sA = buf;
             const bf16_t* sB = buf + kTileElems;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[set][i] = BK ? as_bf16x8(*reinterpret_cast<const uint4*>(
-                                      sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]))
-                                : mn_frag(reinterpret_cast<const char*>(sB) + trb[i] + ks * 16 * 512);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                fb[set][j] = AK ? as_bf16x8(*reinterpret_cast<const uint4*>(
-                                      sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]))
-                                : mn_frag(reinterpret_cast<const char*>(sA) + tra[j] + ks * 16 * 512);
+            rd_a(sB, ks, set, 0);
+            rd_b(sA, ks, set, 0);
+            rd_b(sA, ks, set, 1);
+            rd_a(sB, ks, set, 1);
+            rd_a(sB, ks, set, 2);
+            rd_a(sB, ks, set, 3);
         };
         for (int kt = 0; kt < nk; ++kt) {
             bf16_t* cur = (kt & 1) ? lds1 : lds0;
@@ -513,14 +522,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
                 // interleave the next step's fragment reads with this step's
-                // products: MFMA, read, MFMA, read, ...
+                // products: MFMA, read(s), MFMA, read(s), ... (a fragment is
+                // one read k-major, two transpose reads mn-major)
                 if (ks + 1 < kTK / 16) {
+                    constexpr int kReadsPerMfma = AK && BK ? 1 : 2;
 #pragma unroll
-                    for (int x = 0; x < (AK && BK ? 6 : 12); ++x) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    for (int x = 0; x < 6; ++x) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerMfma, 0);  // reads
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);       // the rest
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // the rest
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
