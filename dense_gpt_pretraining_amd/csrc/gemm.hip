@@ -364,6 +364,72 @@ __device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64
             make_uint2(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]));
 }
 
+// sum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1): every lane
+// of the row ends with the same value
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xF, 0xF, true));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xF, 0xF, true));
+    return v;
+}
+
+// The same for head_dim 128, where a wave's 128 columns are one head: 16
+// lanes take one row, lane l the columns 4 l .. +3 and their rotation
+// partners 64 + 4 l .. +3, so the rotation needs no exchange and the head's
+// sum of squares is one 16-lane DPP reduction.  `stage` holds the wave's 32
+// rows x 128 columns (16-byte chunk c of row r at chunk position c ^ r).
+__device__ __forceinline__ void qkv_rope_pass128(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
+                                                 int N, const float* stage, int mrow0,
+                                                 int ncol0, int lane) {
+    if (ncol0 >= N) return;
+    const int H = e.n_head;
+    const int head = ncol0 >> 7;
+    const bool rot = head <= H;
+    const int l16 = lane & 15, rsub = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int row = 4 * t + rsub;
+        const int mi = mrow0 + row;
+        const float4 a = *reinterpret_cast<const float4*>(stage + row * 128 + ((l16 ^ row) << 2));
+        const float4 b =
+            *reinterpret_cast<const float4*>(stage + row * 128 + (((16 + l16) ^ row) << 2));
+        const bool valid = mi < M;
+        const float rs = valid ? e.rowscale[mi] : 0.f;
+        float x1[4] = {a.x * rs, a.y * rs, a.z * rs, a.w * rs};
+        float x2[4] = {b.x * rs, b.y * rs, b.z * rs, b.w * rs};
+        if (rot) {
+            const int pos = valid ? mi % e.seq_len : 0;
+            const float4 c4 = *reinterpret_cast<const float4*>(e.cos_t + pos * 64 + 4 * l16);
+            const float4 s4 = *reinterpret_cast<const float4*>(e.sin_t + pos * 64 + 4 * l16);
+            const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+            float ss = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float y1 = x1[q] * cs[q] - x2[q] * sn[q];
+                const float y2 = x1[q] * sn[q] + x2[q] * cs[q];
+                x1[q] = y1;
+                x2[q] = y2;
+                ss += y1 * y1 + y2 * y2;
+            }
+            ss = row16_sum(ss);
+            const float rr = __builtin_amdgcn_rsqf(ss * (1.f / 128.f) + e.eps);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                x1[q] *= rr;
+                x2[q] *= rr;
+            }
+            if (valid && l16 == 0) e.rqk[(int64_t)mi * (H + 1) + head] = rr;
+        }
+        if (valid) {
+            bf16_t* o = C + (int64_t)mi * ldc + ncol0 + 4 * l16;
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf2(x1[0], x1[1]), pack_bf2(x1[2], x1[3]));
+            *reinterpret_cast<uint2*>(o + 64) =
+                make_uint2(pack_bf2(x2[0], x2[1]), pack_bf2(x2[2], x2[3]));
+        }
+    }
+}
+
 // 512 threads: wave w owns m rows wm*64 .. +63 (wm = w & 3) and n rows
 // wn*128 .. +127 (wn = w >> 2) of the 256 x 256 tile: 2 x 4 accumulator blocks.
 // In a k-major tile, fragment row 32 i + (lane & 31) of a 32-aligned block
@@ -579,6 +645,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             }
         __syncthreads();
         const int64_t n = n0 + wn * 128 + 4 * li;
+        if (MODE == EPI_QKV_ROPE && e.head_dim == 128) {
+            qkv_rope_pass128(e, static_cast<bf16_t*>(C), ldc, M, N, stage, m0 + wm * 64 + 32 * j,
+                             n0 + wn * 128, lane);
+        } else
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int row = 2 * t + hi;
