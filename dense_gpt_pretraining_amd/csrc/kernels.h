@@ -124,7 +124,7 @@ hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk,
                            const float* sin_t, T* dqkv, hipStream_t s);
 // dres += dn - r^2 * x * mean(dn * x) over each row; dres_t = (T)dres
 template <typename T>
-hipError_t norm_bwd_resid(const float* dn, const T* x, const float* r, int N,
+hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N,
                           int D, float* dres, T* dres_t, hipStream_t s);
 // de[t] = r0[t]*dh[t] - r0[t]^3 * e[t] * mean(dh[t]*e[t]), e[t] = wte[tok[t]]
 template <typename T>

@@ -157,21 +157,22 @@ __global__ __launch_bounds__(kRowThreads) void k_rope_qknorm_bwd(
 
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
-    const float* __restrict__ dn, const T* __restrict__ x,
+    const T* __restrict__ dn, const T* __restrict__ x,
     const float* __restrict__ r, int N, int D, float* __restrict__ dres,
     T* __restrict__ dres_t) {
     constexpr int V = Elt<T>::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= N) return;
-    const float* g = dn + row * D;
+    const T* g = dn + row * D;
     const T* xr = x + row * D;
     float dot = 0.f;
     for (int c = lane * V; c < D; c += kWave * V) {
-        float xv[V];
+        float xv[V], gv[V];
         ld_vec<T>(xr + c, xv);
+        ld_vec<T>(g + c, gv);
 #pragma unroll
-        for (int k = 0; k < V; ++k) dot += g[c + k] * xv[k];
+        for (int k = 0; k < V; ++k) dot += gv[k] * xv[k];
     }
     dot = wave_sum(dot);
     const float rr = r[row];
@@ -179,10 +180,11 @@ __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     float* d = dres + row * D;
     T* dt = dres_t + row * D;
     for (int c = lane * V; c < D; c += kWave * V) {
-        float xv[V], o[V];
+        float xv[V], gv[V], o[V];
         ld_vec<T>(xr + c, xv);
+        ld_vec<T>(g + c, gv);
 #pragma unroll
-        for (int k = 0; k < V; ++k) o[k] = d[c + k] + g[c + k] - coef * xv[k];
+        for (int k = 0; k < V; ++k) o[k] = d[c + k] + gv[k] - coef * xv[k];
 #pragma unroll
         for (int k = 0; k < V; ++k) d[c + k] = o[k];
         st_vec<T>(dt + c, o);
@@ -468,7 +470,7 @@ hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk, const
 }
 
 template <typename T>
-hipError_t norm_bwd_resid(const float* dn, const T* x, const float* r, int N, int D,
+hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D,
                           float* dres, T* dres_t, hipStream_t s) {
     hipLaunchKernelGGL(k_norm_bwd_resid<T>, dim3(row_blocks(N)), dim3(kRowThreads), 0, s, dn, x,
                        r, N, D, dres, dres_t);
@@ -556,7 +558,7 @@ hipError_t count_bad_ids(const int32_t* a, const int32_t* b, int64_t n, int V, i
     template hipError_t rope_qknorm_bwd<T>(const T*, const float*, const float*, const float*, \
                                            const float*, const float*, int, int, int, int,     \
                                            const float*, const float*, T*, hipStream_t);       \
-    template hipError_t norm_bwd_resid<T>(const float*, const T*, const float*, int, int,     \
+    template hipError_t norm_bwd_resid<T>(const T*, const T*, const float*, int, int,     \
                                           float*, T*, hipStream_t);                            \
     template hipError_t embed_bwd_rows<T>(const float*, const T*, const int32_t*,             \
                                           const float*, int, int, float*, hipStream_t);        \

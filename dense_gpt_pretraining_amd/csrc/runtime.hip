@@ -370,20 +370,22 @@ struct Step {
         const size_t skb = p.splitk_bytes;
         float* dres = at<float>(p.dres);
         T* dres_t = at<T>(p.dres_t);
-        float* dn = at<float>(p.dn);
+        // data gradient entering a norm backward, stored as T (the buffer
+        // keeps fp32 size: the embedding backward reuses it as fp32 de)
+        T* dn = at<T>(p.dn);
         T* z = at<T>(p.z);  // now holds r_f/N * dloss/dz
         auto G_of = [&](int idx) { return grads + lay[idx].offset; };
         // norm backward with residual: reads dn, x, dres; writes dres, dres_t
-        const double nbb = (double)N * D * (4 + es() + 4 + 4 + es()) + N * 4.0;
+        const double nbb = (double)N * D * (es() + es() + 4 + 4 + es()) + N * 4.0;
         auto tb = [&](int64_t r, int64_t k) { return 2.0 * r * k * es(); };
 
         // head: df' = dz' W_lm, dW_lm = dz'^T h_L
         T* hL = X(L);
         NC_RUN("transpose_w", 0, tb(V, D),
                nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
-        NC_RUN("gemm_nt_f32", gf(N, D, V), gb(N, D, V, 4.0),
+        NC_RUN("gemm_nt_dn", gf(N, D, V), gb(N, D, V, es()),
                nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
-                           epi(nc::EPI_STORE_F32), nullptr, 0, s));
+                           epi(nc::EPI_STORE_T), nullptr, 0, s));
         NC_RUN("gemm_tn_f32", gf(V, D, N), gb(V, D, N, 4.0),
                nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
                            epi(nc::EPI_STORE_F32), sk, skb, s));
@@ -413,9 +415,9 @@ struct Step {
                                G_of(i_layer(l, 5)), F, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("transpose_w", 0, tb(F, D),
                    nc::transpose<T>(W(i_layer(l, 4)), (int)F, (int)D, D, wt, F, s));
-            NC_RUN("gemm_nt_f32", gf(N, D, F), gb(N, D, F, 4.0),
+            NC_RUN("gemm_nt_dn", gf(N, D, F), gb(N, D, F, es()),
                    nc::gemm<T>((int)N, (int)D, (int)F, dgu, F, true, wt, F, true, dn, D,
-                               epi(nc::EPI_STORE_F32), nullptr, 0, s));
+                               epi(nc::EPI_STORE_T), nullptr, 0, s));
             NC_RUN("gemm_tn_f32", gf(F, D, N), gb(F, D, N, 4.0),
                    nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
                                G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
@@ -466,9 +468,9 @@ struct Step {
             }
             NC_RUN("transpose_w", 0, tb(Wq, D),
                    nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
-            NC_RUN("gemm_nt_f32", gf(N, D, Wq), gb(N, D, Wq, 4.0),
+            NC_RUN("gemm_nt_dn", gf(N, D, Wq), gb(N, D, Wq, es()),
                    nc::gemm<T>((int)N, (int)D, (int)Wq, dqkv, Wq, true, wt, Wq, true, dn, D,
-                               epi(nc::EPI_STORE_F32), nullptr, 0, s));
+                               epi(nc::EPI_STORE_T), nullptr, 0, s));
             NC_RUN("gemm_tn_f32", gf(Wq, D, N), gb(Wq, D, N, 4.0),
                    nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
                                G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
@@ -476,7 +478,7 @@ struct Step {
                    nc::norm_bwd_resid<T>(dn, x, R1(l), (int)N, (int)D, dres, dres_t, s));
         }
         // embedding: h0 = r0 e, e = W_te[tok]
-        float* de = dn;
+        float* de = at<float>(p.dn);
         NC_RUN("embed_bwd_rows", 0, N * D * (4.0 + es() + 4.0),
                nc::embed_bwd_rows<T>(dres, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de,
                                      s));
