@@ -247,9 +247,12 @@ __device__ __forceinline__ void barrier_nofence() {
 
 __device__ __forceinline__ int xcd_remap(int pid, int total) {
     // consecutive workgroup ids land on different XCDs (round robin over 8);
-    // give each XCD a contiguous range of tiles so neighbours share its L2
-    if (total % 8 != 0) return pid;
-    return (pid % 8) * (total / 8) + pid / 8;
+    // give each XCD a contiguous range of work items so neighbours share its
+    // L2: XCD x takes q + (x < r) items starting at x q + min(x, r), with
+    // total = 8 q + r (a bijection of [0, total))
+    const int q = total >> 3, r = total & 7;
+    const int x = pid & 7, local = pid >> 3;
+    return x * q + min(x, r) + local;
 }
 
 template <int MODE>
@@ -438,6 +441,7 @@ __device__ __forceinline__ void qkv_rope_pass128(const EpiDev& e, bf16_t* C, int
 // (foff) and every fragment read is base + constant.
 template <bool AK, bool BK, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, int k_per_split,
+                                                           int nsplit,
                                                            const bf16_t* __restrict__ A,
                                                            int64_t lda,
                                                            const bf16_t* __restrict__ B,
@@ -450,7 +454,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
 
     const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     const int total = tiles_m * tiles_n;
-    const int pid = xcd_remap(blockIdx.x, total);
+    // one work item per (k split, tile), split-major, spread over the XCDs
+    // in contiguous ranges
+    const int item = xcd_remap(blockIdx.x, total * nsplit);
+    const int split = item / total;
+    const int pid = item - split * total;
     // grouped order: 8 m-tiles share a column sweep over n
     constexpr int kGroup = 8;
     const int group = pid / (kGroup * tiles_n);
@@ -460,10 +468,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     const int tn = (pid % (kGroup * tiles_n)) / gsize;
     const int m0 = tm * kTM, n0 = tn * kTN;
 
-    const int kb = blockIdx.z * k_per_split;
+    const int kb = split * k_per_split;
     const int ke = min(K, kb + k_per_split);
     if (MODE == EPI_STORE_F32 && split_stride)
-        C = static_cast<float*>(C) + blockIdx.z * split_stride;
+        C = static_cast<float*>(C) + split * split_stride;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -710,8 +718,9 @@ hipError_t launch_mfma(int M, int N, int K, const bf16_t* A, int64_t lda, const 
     k_per = (int)ceil_div(k_per, kTK) * kTK;
     const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
     auto kern = k_gemm_mfma<AK, BK, MODE>;
-    hipLaunchKernelGGL(kern, dim3(tiles, 1, splits), dim3(kThreads), 0, s, M, N, K, k_per, A, lda,
-                       B, ldb, C, ldc, e, split_stride);
+    // one workgroup per (split, tile) item
+    hipLaunchKernelGGL(kern, dim3(tiles * splits, 1, 1), dim3(kThreads), 0, s, M, N, K, k_per,
+                       splits, A, lda, B, ldb, C, ldc, e, split_stride);
     return hipGetLastError();
 }
 
