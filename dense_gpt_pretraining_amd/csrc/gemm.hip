@@ -25,7 +25,7 @@
 // 4 consecutive n of one row m in each lane's accumulator registers: the
 // epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
 // Tiles are visited XCD by XCD (each of the 8 dies gets a contiguous range)
-// and in groups of 8 m-tiles, so the operand rows they share stay in L2.
+// and in groups of 4 m-tiles, so the operand rows they share stay in L2.
 //
 // fp32: a plain LDS-tiled SIMT kernel (64 x 64 tiles, 4 x 4 per thread).
 #include "kernels.h"
@@ -459,8 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     const int item = xcd_remap(blockIdx.x, total * nsplit);
     const int split = item / total;
     const int pid = item - split * total;
-    // grouped order: 8 m-tiles share a column sweep over n
-    constexpr int kGroup = 8;
+    // grouped order: 4 m-tiles share a column sweep over n (of 2, 3, 4, 6, 8,
+    // 16 and 32 the fastest over the whole training step)
+    constexpr int kGroup = 4;
     const int group = pid / (kGroup * tiles_n);
     const int first_m = group * kGroup;
     const int gsize = min(tiles_m - first_m, kGroup);
