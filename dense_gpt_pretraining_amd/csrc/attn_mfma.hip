@@ -788,8 +788,18 @@ int kv_slots_per_seq(int T, int H, int chunk_rows) {
     return s;
 }
 
-constexpr int kChunkRows = 2048;
-static_assert(kChunkRows % kQT == 0, "chunks hold whole row tiles");
+// Rows per dK/dV chunk.  With at least two key blocks per compute unit the
+// blocks alone balance the machine (heaviest first: block kb sees (n_kb - kb)
+// row tiles, so early finishers pick up the light blocks), and each block
+// takes all of its rows in one chunk; otherwise chunks of 2048 rows add the
+// parallelism.  Either way a multiple of the row tile.
+constexpr int kChunkRowsSmall = 2048;
+static_assert(kChunkRowsSmall % kQT == 0, "chunks hold whole row tiles");
+int chunk_rows(int B, int T, int H) {
+    const int64_t blocks = (int64_t)B * ((T + kKB - 1) / kKB);
+    if (blocks >= 512) return (int)(((int64_t)T * H + kQT - 1) / kQT * kQT);
+    return kChunkRowsSmall;
+}
 
 template <int HD>
 hipError_t launch_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
@@ -809,7 +819,8 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const AttnBwdFuse fz = fuse ? *fuse : AttnBwdFuse{};
     // scratch: delta [B*T*H], then the dK and dV partials
     float* delta = scratch;
-    const int slots = kv_slots_per_seq(T, H, kChunkRows);
+    const int chunk = chunk_rows(B, T, H);
+    const int slots = kv_slots_per_seq(T, H, chunk);
     const int64_t part = (int64_t)B * slots * kKB * HD;
     float* dk_part = scratch + ceil_div((int64_t)B * T * H, 64) * 64;
     float* dv_part = dk_part + part;
@@ -843,7 +854,7 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(512), 0, s, q, k, v, ldq,
                        ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2, scale,
-                       kChunkRows, slots);
+                       chunk, slots);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = prof_cut("attn_dkv_reduce", 0, part_b + 2.0 * toks * HD * 4.0);
@@ -851,11 +862,11 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const int64_t n4 = (int64_t)B * T * (HD / 4);
     if (fuse)
         hipLaunchKernelGGL((k_attn_dkv_reduce<HD, true>), dim3((unsigned)ceil_div(n4, 256)),
-                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots,
+                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, chunk, slots,
                            ldq, fz);
     else
         hipLaunchKernelGGL((k_attn_dkv_reduce<HD, false>), dim3((unsigned)ceil_div(n4, 256)),
-                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, kChunkRows, slots,
+                           dim3(256), 0, s, dk_part, dv_part, dk, dv, B, T, H, chunk, slots,
                            ldq, fz);
     return hipGetLastError();
 }
@@ -887,7 +898,7 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
 
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd) {
     const int64_t delta = ceil_div((int64_t)B * T * H, 64) * 64;
-    const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, kChunkRows) * kKB * hd;
+    const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, chunk_rows(B, T, H)) * kKB * hd;
     return (size_t)(delta + 2 * part) * sizeof(float);
 }
 
