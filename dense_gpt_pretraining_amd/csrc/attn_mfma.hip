@@ -473,12 +473,19 @@ __host__ __device__ __forceinline__ int kv_chunks(int kb, int H, int rows_total,
     return (rows_total - kv_rows_begin(kb, H) + chunk_rows - 1) / chunk_rows;
 }
 
-template <int HD>
+// Output of the dK/dV kernel: per-chunk fp32 partials (summed by
+// k_attn_dkv_reduce), or -- when each key block is one chunk -- the finished
+// rows: fp32 dk, dv, or the fused tail (key QK-norm and rotary backward, bf16
+// into the qkv-shaped gradient, as k_attn_dkv_reduce<HD, true> does).
+enum { kDkvPartials = 0, kDkvDirect = 1, kDkvFused = 2 };
+
+template <int HD, int OUT>
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dk_part, float* __restrict__ dv_part,
-    int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq) {
+    int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq,
+    AttnBwdFuse fz) {
     constexpr int TQ = kQT * HD * 2;              // bytes of a Q (or dO) row tile
     constexpr int RPI = 1024 / (HD * 2);          // tile rows per copy instruction
     constexpr int NI = TQ / 1024 / 8;             // copy instructions per wave per tile
@@ -697,6 +704,92 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
         for (int db = 0; db < HD / 32; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) dva[db][r] += xch[(db * 16 + r) * 64 + lane];
+        if constexpr (OUT != kDkvPartials) {
+            // lane holds key `key`, elements d = 32 db + 8 gq + 4 g + e; the
+            // rotation partner d +- HD/2 is register block db +- HD/64 of the
+            // same lane, the other half of the row is in lane ^ 32
+            const int64_t tok = seq0 + key;
+            if constexpr (OUT == kDkvDirect) {
+#pragma unroll
+                for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int d = 32 * db + 8 * gq + 4 * g;
+                        *reinterpret_cast<float4*>(dk_part + tok * HD + d) =
+                            make_float4(dka[db][4 * gq] * scale, dka[db][4 * gq + 1] * scale,
+                                        dka[db][4 * gq + 2] * scale, dka[db][4 * gq + 3] * scale);
+                        *reinterpret_cast<float4*>(dv_part + tok * HD + d) =
+                            make_float4(dva[db][4 * gq], dva[db][4 * gq + 1], dva[db][4 * gq + 2],
+                                        dva[db][4 * gq + 3]);
+                    }
+            } else {
+                const float sc = fz.r1[tok];
+                const bf16_t* yk = fz.y + tok * ldq + (int64_t)H * HD;
+                float dot = 0.f;
+#pragma unroll
+                for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const uint2 w2 =
+                            *reinterpret_cast<const uint2*>(yk + 32 * db + 8 * gq + 4 * g);
+                        const float y[4] = {bf_lo(w2.x), bf_hi(w2.x), bf_lo(w2.y), bf_hi(w2.y)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            dka[db][4 * gq + e] *= scale;
+                            dot += dka[db][4 * gq + e] * y[e];
+                        }
+                    }
+                dot += __shfl_xor(dot, 32, 64);
+                const float rr = fz.rqk[tok * (H + 1) + H], mean = dot / (float)HD;
+#pragma unroll
+                for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const uint2 w2 =
+                            *reinterpret_cast<const uint2*>(yk + 32 * db + 8 * gq + 4 * g);
+                        const float y[4] = {bf_lo(w2.x), bf_hi(w2.x), bf_lo(w2.y), bf_hi(w2.y)};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            dka[db][4 * gq + e] = rr * (dka[db][4 * gq + e] - y[e] * mean);
+                    }
+                constexpr int HALF = HD / 2, DBH = HD / 64;
+                const int kk = key;   // position in the sequence
+                bf16_t* out = fz.dqkv + tok * ldq + (int64_t)H * HD;
+#pragma unroll
+                for (int db = 0; db < DBH; ++db)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int i = 32 * db + 8 * gq + 4 * g;   // < HALF
+                        const float4 c4 =
+                            *reinterpret_cast<const float4*>(fz.cos_t + (int64_t)kk * HALF + i);
+                        const float4 s4 =
+                            *reinterpret_cast<const float4*>(fz.sin_t + (int64_t)kk * HALF + i);
+                        const float cs[4] = {c4.x, c4.y, c4.z, c4.w};
+                        const float sn[4] = {s4.x, s4.y, s4.z, s4.w};
+                        float lo[4], hi[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float a0 = dka[db][4 * gq + e], a1 = dka[db + DBH][4 * gq + e];
+                            lo[e] = sc * (a0 * cs[e] + a1 * sn[e]);
+                            hi[e] = sc * (a1 * cs[e] - a0 * sn[e]);
+                        }
+                        *reinterpret_cast<uint2*>(out + i) =
+                            make_uint2(pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]));
+                        *reinterpret_cast<uint2*>(out + i + HALF) =
+                            make_uint2(pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3]));
+                    }
+#pragma unroll
+                for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int d = 32 * db + 8 * gq + 4 * g;
+                        *reinterpret_cast<uint2*>(out + HD + d) =
+                            make_uint2(pack_bf2(sc * dva[db][4 * gq], sc * dva[db][4 * gq + 1]),
+                                       pack_bf2(sc * dva[db][4 * gq + 2], sc * dva[db][4 * gq + 3]));
+                    }
+            }
+            return;
+        }
         const int64_t pslot = ((int64_t)b * slots_per_seq + slot) * kKB + 32 * wk + li;
         float* okr = dk_part + pslot * HD;
         float* ovr = dv_part + pslot * HD;
@@ -848,13 +941,31 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
                            fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dkv: S, dP, dV and dK; writes one partial per chunk
+    // dkv: S, dP, dV and dK; with one chunk per key block it finishes the
+    // rows itself, otherwise it writes one partial per chunk
+    const bool direct = slots == (T + kKB - 1) / kKB;
+    if (direct) {
+        // finished rows: fp32 dk, dv, or the fused tail into bf16 dqkv
+        const double out_b = fuse ? 2.0 * toks * HD * 2.0 + toks * HD * 2.0 + toks * (4.0 + 4.0)
+                                  : 2.0 * toks * HD * 4.0;
+        e = prof_cut("attn_bwd_dkv", 4 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows + out_b);
+        if (e != hipSuccess) return e;
+        if (fuse)
+            hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvFused>), dim3(slots * B), dim3(512), 0,
+                               s, q, k, v, ldq, ldkv, dout, lse, delta, dk, dv, B, T, H,
+                               scale_log2, scale, chunk, slots, fz);
+        else
+            hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvDirect>), dim3(slots * B), dim3(512),
+                               0, s, q, k, v, ldq, ldkv, dout, lse, delta, dk, dv, B, T, H,
+                               scale_log2, scale, chunk, slots, fz);
+        return hipGetLastError();
+    }
     const double part_b = 2.0 * B * slots * kKB * HD * 4.0;
     e = prof_cut("attn_bwd_dkv", 4 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows + part_b);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_bwd_dkv_mfma<HD>, dim3(slots * B), dim3(512), 0, s, q, k, v, ldq,
-                       ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2, scale,
-                       chunk, slots);
+    hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvPartials>), dim3(slots * B), dim3(512), 0, s,
+                       q, k, v, ldq, ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2,
+                       scale, chunk, slots, fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = prof_cut("attn_dkv_reduce", 0, part_b + 2.0 * toks * HD * 4.0);

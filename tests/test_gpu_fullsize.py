@@ -106,6 +106,35 @@ def test_full_size_gradients_on_a_repeated_sequence(name):
 
 
 @pytest.mark.timeout(600)
+def test_gradients_with_one_dkv_chunk_per_key_block():
+    """A d20 block at batch 256 x 256 positions has 512 key blocks, so the
+    dK/dV kernel finishes each block's rows itself, with the key QK-norm and
+    rotary backward fused in; gradients of a repeated sequence against the
+    oracle's gradient of that sequence."""
+    torch = require_gpu()
+    cfg = get_config("d20", n_layer=1, seq_len=256, batch=256)
+    m = _model(cfg)
+    p, params = _device_params(m, cfg)
+    tokens, targets = make_tokens(cfg)
+    B = cfg["batch"]
+    tok = np.repeat(tokens[-1:], B, axis=0)
+    tgt = np.repeat(targets[-1:], B, axis=0)
+    loss, grads = m.forward_backward(p, tok, tgt)
+    torch.cuda.synchronize()
+    got_loss = float(loss.item())
+    g = m.unpack(grads)
+    del grads
+    ocfg = get_config("d20", n_layer=1, seq_len=256, batch=1)
+    want_loss, want = oracle.forward_backward(ocfg, params, tok[:1], tgt[:1])
+    assert abs(got_loss - want_loss) <= 1e-2 * abs(want_loss)
+    for k in want:
+        e, c = rel_l2(g[k], want[k]), cosine(g[k], want[k])
+        print(f"{k}: rel-L2 {e:.2e} cos {c:.6f}")
+        assert e < 3e-2, (k, e)
+        assert c >= 0.999, (k, c)
+
+
+@pytest.mark.timeout(600)
 def test_attention_at_the_long_configuration_shape():
     """nc_op_attention_fwd/bwd with B=8, T=8192, H=10, hd=128 (the long
     configuration); the last sequence is compared with the oracle."""

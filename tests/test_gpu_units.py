@@ -135,6 +135,45 @@ def test_attention_forward_backward(dtype, Bn, T, H, hd):
     assert rel_l2(from_dev(dv), np.concatenate(wv)) < tolb
 
 
+@pytest.mark.parametrize("Bn,T,H,hd", [(512, 128, 2, 64), (256, 256, 2, 128)])
+def test_attention_backward_one_chunk_per_key_block(Bn, T, H, hd):
+    """With at least 512 key blocks in the batch the dK/dV kernel takes every
+    row of a key block in one chunk and writes dk, dv itself (no partials);
+    sampled sequences against the oracle, every output finite."""
+    torch = require_gpu()
+    b = _b()
+    dtype = "bf16"
+    q, k, v = _qkv(Bn, T, H, hd, dtype, 11)
+    do = rand((Bn * T, H, hd), 21, dtype=dtype)
+    ld = (H + 2) * hd
+    buf = to_dev(_pack_qkv(q, k, v), dtype)
+    base = buf.data_ptr()
+    o = torch.empty((Bn * T, H * hd), dtype=buf.dtype, device="cuda")
+    lse = torch.empty(Bn * T * H, dtype=torch.float32, device="cuda")
+    b.nc_op_attention_fwd(1, Bn, T, H, hd, base, base + H * hd * 2, base + (H + 1) * hd * 2, ld,
+                          ld, o.data_ptr(), lse.data_ptr(), stream())
+    dod = to_dev(do.reshape(Bn * T, H * hd), dtype)
+    nsc = b.nc_op_attention_bwd_scratch_bytes(Bn, T, H, hd)
+    scratch = torch.empty(nsc, dtype=torch.uint8, device="cuda")
+    dq = torch.empty((Bn * T, H, hd), dtype=torch.float32, device="cuda")
+    dk = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
+    dv = torch.empty((Bn * T, hd), dtype=torch.float32, device="cuda")
+    b.nc_op_attention_bwd(1, Bn, T, H, hd, base, base + H * hd * 2, base + (H + 1) * hd * 2, ld,
+                          ld, o.data_ptr(), dod.data_ptr(), lse.data_ptr(), scratch.data_ptr(),
+                          nsc, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), stream())
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+    gq, gk, gv = from_dev(dq), from_dev(dk), from_dev(dv)
+    for i in (0, Bn // 2 + 1, Bn - 1):
+        sl = slice(i * T, (i + 1) * T)
+        a, bb, c = oracle.causal_mqa_attention_backward(
+            q[sl].astype(np.float64), k[sl].astype(np.float64), v[sl].astype(np.float64),
+            do[sl].astype(np.float64))
+        assert rel_l2(gq[sl], a) < 1e-2, i
+        assert rel_l2(gk[sl], bb) < 1e-2, i
+        assert rel_l2(gv[sl], c) < 1e-2, i
+
+
 @pytest.mark.parametrize("dtype,V,ldz", [("bf16", 50257, 50432), ("bf16", 65536, 65536),
                                           ("f32", 512, 512), ("bf16", 700, 768)])
 def test_softcap_cross_entropy(dtype, V, ldz):
