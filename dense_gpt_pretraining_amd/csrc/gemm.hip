@@ -606,16 +606,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
                 // interleave the next step's fragment reads with this step's
-                // products: MFMA, read(s), MFMA, read(s), ... (a fragment is
-                // one read k-major, two transpose reads mn-major)
+                // products (a fragment is one read k-major, two transpose
+                // reads mn-major): k-major 2 MFMAs, 2 reads, ...; mn-major
+                // 1 MFMA, 3 reads, ... (the fastest of the patterns tried
+                // over the whole step)
                 if (ks + 1 < kTK / 16) {
-                    constexpr int kReadsPerMfma = AK && BK ? 1 : 2;
+                    constexpr int kGroups = AK && BK ? 3 : 4;
+                    constexpr int kMfmaPerGroup = AK && BK ? 2 : 1;
+                    constexpr int kReadsPerGroup = AK && BK ? 2 : 3;
 #pragma unroll
-                    for (int x = 0; x < 6; ++x) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-                        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerMfma, 0);  // reads
+                    for (int x = 0; x < kGroups; ++x) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerGroup, 0);   // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, kReadsPerGroup, 0);  // reads
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);       // the rest
+                    __builtin_amdgcn_sched_group_barrier(0x008, 8 - kGroups * kMfmaPerGroup,
+                                                         0);                             // the rest
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
