@@ -14,13 +14,15 @@
 // distinct banks (the bank-conflict counter reads zero).
 //   Both operands go straight from global memory into LDS
 //   (buffer loads with the LDS bit, no staging registers); the loads of tile k+1
-//   are in flight while tile k is multiplied, and the fragments of k step
-//   s+1 are read while the matrix instructions of step s issue.
+//   are in flight while tile k is multiplied.
 //   k-major tiles are stored 256 rows x 64 k and a fragment is one 16-byte
-//   read; mn-major tiles (the weight-gradient layout) are stored as they lie
-//   in memory, 64 k x 256 rows, and a fragment (8 consecutive k of one row)
-//   is two LDS transpose reads (ds_read_b64_tr_b16), so no layout is ever
-//   transposed in registers.
+//   read; the fragments of k step s+1 are read while the matrix instructions
+//   of step s issue.  mn-major tiles (the weight-gradient layout) are stored
+//   as they lie in memory, 64 k x 256 rows, and a fragment (8 consecutive k
+//   of one row) is two LDS transpose reads (ds_read_b64_tr_b16), so no layout
+//   is ever transposed in registers; all of a tile's transpose reads are
+//   issued before the next tile's copy (the compiler would otherwise wait for
+//   the copy before each of them).
 // The MFMA "A" side takes the n rows and the "B" side the m rows, which puts
 // 4 consecutive n of one row m in each lane's accumulator registers: the
 // epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
@@ -593,6 +595,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                 wait_vmem();
                 barrier_nofence();
             }
+            if constexpr (!AK) {
+                // mn-major: every transpose read of the tile is issued before
+                // the next tile's copy.  (The compiler cannot tell that a
+                // transpose read does not alias an LDS copy in flight and
+                // would wait for the copy before each one.)
+                bf16x8_t ga[kTK / 16][4], gb[kTK / 16][2];
+                const char* sA = reinterpret_cast<const char*>(cur);
+                const char* sB = reinterpret_cast<const char*>(cur + kTileElems);
+#pragma unroll
+                for (int ks = 0; ks < kTK / 16; ++ks) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ga[ks][i] = mn_frag(sB + trb[i] + ks * 16 * 512);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) gb[ks][j] = mn_frag(sA + tra[j] + ks * 16 * 512);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (kt + 1 < nk) issue(kt + 1, nxt);
+                else if (kPre) load_aux(0, aux0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < kTK / 16; ++ks)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = mfma32(ga[ks][i], gb[ks][j], acc[i][j]);
+                continue;
+            }
             if (kt + 1 < nk) issue(kt + 1, nxt);
             else if (kPre) load_aux(0, aux0);
             rd(cur, 0, 0);
@@ -606,14 +636,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
                 // interleave the next step's fragment reads with this step's
-                // products (a fragment is one read k-major, two transpose
-                // reads mn-major): k-major 2 MFMAs, 2 reads, ...; mn-major
-                // 1 MFMA, 3 reads, ... (the fastest of the patterns tried
-                // over the whole step)
+                // products: 2 MFMAs, 2 reads, ... (the fastest of the
+                // patterns tried over the whole step)
                 if (ks + 1 < kTK / 16) {
-                    constexpr int kGroups = AK && BK ? 3 : 4;
-                    constexpr int kMfmaPerGroup = AK && BK ? 2 : 1;
-                    constexpr int kReadsPerGroup = AK && BK ? 2 : 3;
+                    constexpr int kGroups = 3;
+                    constexpr int kMfmaPerGroup = 2;
+                    constexpr int kReadsPerGroup = 2;
 #pragma unroll
                     for (int x = 0; x < kGroups; ++x) {
                         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerGroup, 0);   // MFMA
