@@ -531,13 +531,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, buf + kTileElems, wave);
         else mn_issue(B + (int64_t)k0 * ldb + n0, mb, buf + kTileElems, wave);
     };
-    // epilogue aux rows of the first 32-row pass (g of the relu^2 backward),
-    // requested during the last k tile so that their latency hides behind its
-    // products
+    // the epilogue's aux rows (x of the residual, g of the relu^2 backward)
     constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
     const int li = lane & 31, hi = lane >> 5;
     const bool full_n = n0 + kTN <= N;
-    uint2 aux0[16];
     auto load_aux = [&](int j, uint2 (&dst)[16]) {
         const int64_t n = n0 + wn * 128 + 4 * li;
         const bool nok = full_n || n + 3 < N;
@@ -550,9 +547,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                                                          m * ldc + n);
         }
     };
-    // (the residual epilogue keeps its registers for the main loop instead)
-    constexpr bool kPre = MODE == EPI_RELU2_BWD;
-    if (kPre && nk == 0) load_aux(0, aux0);
     if (nk > 0) {
         issue(0, lds0);
         wait_vmem();
@@ -612,7 +606,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 if (kt + 1 < nk) issue(kt + 1, nxt);
-                else if (kPre) load_aux(0, aux0);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < kTK / 16; ++ks)
@@ -623,9 +616,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                             acc[i][j] = mfma32(ga[ks][i], gb[ks][j], acc[i][j]);
                 continue;
             }
-            if (kt + 1 < nk) issue(kt + 1, nxt);
-            else if (kPre) load_aux(0, aux0);
-            rd(cur, 0, 0);
+            if (kt == 0) {
+                // first tile: its first fragments are read before the next
+                // tile's copy is issued (the compiler would wait for that copy
+                // before the reads)
+                rd(cur, 0, 0);
+                if (kt + 1 < nk) issue(kt + 1, nxt);
+            } else {
+                if (kt + 1 < nk) issue(kt + 1, nxt);
+                rd(cur, 0, 0);
+            }
 #pragma unroll
             for (int ks = 0; ks < kTK / 16; ++ks) {
                 const int cs = ks & 1;
@@ -668,17 +668,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         // the pass's epilogue inputs are requested before the LDS round trip
-        // (the first pass's aux rows already are)
         uint2 auxv[16];
         float rsv[16];
-        if (kAux) {
-            if (kPre && j == 0) {
-#pragma unroll
-                for (int t = 0; t < 16; ++t) auxv[t] = aux0[t];
-            } else {
-                load_aux(j, auxv);
-            }
-        }
+        if (kAux) load_aux(j, auxv);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
