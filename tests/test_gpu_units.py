@@ -32,6 +32,9 @@ def _b():
     (300, 520, 192, False),     # mn-major, several tiles
     (1, 8, 64, False),          # mn-major, degenerate m, n
     (512, 768, 4096, False),    # long k: split over the k loop
+    (300, 520, 256, True),      # even k-tile count: persistent launch, ragged m and n tails
+    (1, 8, 128, True),          # persistent launch, degenerate m, n
+    (512, 256, 2048, False),    # persistent launch, mn-major whole tiles, k split
 ])
 def test_matmul(dtype, M, N, K, kmajor):
     torch = require_gpu()
