@@ -221,12 +221,14 @@ __global__ __launch_bounds__(kRowThreads) void k_embed_bwd_rows(
     }
 }
 
-// Softcap + cross-entropy, one 256-thread block per row.  The raw row is held
+// Softcap + cross-entropy, one 512-thread block per row (measured faster than
+// 256 or 1024: 16 chunks per thread at a 65536 vocabulary leave room for
+// four waves per SIMD).  The raw row is held
 // in registers (MAXC 16-byte chunks per thread), so logits are read from HBM
 // once and gradients written once.  The softcap bounds every logit to
 // |c| <= s, and the host admits only s <= 60, so sum(exp(c)) cannot overflow
 // fp32 and the log-sum-exp needs no running maximum.
-constexpr int kCeThreads = 256;
+constexpr int kCeThreads = 512;
 
 template <typename T>
 __device__ __forceinline__ void unpack_chunk(const uint4& raw, float* out);
