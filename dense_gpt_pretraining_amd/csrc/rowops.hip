@@ -156,42 +156,6 @@ __global__ __launch_bounds__(kRowThreads) void k_rope_qknorm_bwd(
 }
 
 template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
-    const T* __restrict__ dn, const T* __restrict__ x,
-    const float* __restrict__ r, int N, int D, float* __restrict__ dres,
-    T* __restrict__ dres_t) {
-    constexpr int V = Elt<T>::kVec;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= N) return;
-    const T* g = dn + row * D;
-    const T* xr = x + row * D;
-    float dot = 0.f;
-    for (int c = lane * V; c < D; c += kWave * V) {
-        float xv[V], gv[V];
-        ld_vec<T>(xr + c, xv);
-        ld_vec<T>(g + c, gv);
-#pragma unroll
-        for (int k = 0; k < V; ++k) dot += gv[k] * xv[k];
-    }
-    dot = wave_sum(dot);
-    const float rr = r[row];
-    const float coef = rr * rr * dot / (float)D;
-    float* d = dres + row * D;
-    T* dt = dres_t + row * D;
-    for (int c = lane * V; c < D; c += kWave * V) {
-        float xv[V], gv[V], o[V];
-        ld_vec<T>(xr + c, xv);
-        ld_vec<T>(g + c, gv);
-#pragma unroll
-        for (int k = 0; k < V; ++k) o[k] = d[c + k] + gv[k] - coef * xv[k];
-#pragma unroll
-        for (int k = 0; k < V; ++k) d[c + k] = o[k];
-        st_vec<T>(dt + c, o);
-    }
-}
-
-template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_embed_bwd_rows(
     const float* __restrict__ dh, const T* __restrict__ wte,
     const int32_t* __restrict__ tok, const float* __restrict__ r0, int N, int D,
@@ -248,6 +212,56 @@ __device__ __forceinline__ void unpack_chunk<bf16_t>(const uint4& raw, float* ou
 // so that tanh = 1 - 2r and the softcapped logit is s (1 - 2r).
 __device__ __forceinline__ float tanh_r(float y) {
     return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y * 2.8853900817779268f) + 1.f);
+}
+
+// One wave per row.  The row's x and dn are read once into registers
+// (MAXC 16-byte chunks of each per lane), used for the dot product and again
+// for the output, so HBM sees each input byte once.
+template <typename T, int MAXC>
+__global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
+    const T* __restrict__ dn, const T* __restrict__ x,
+    const float* __restrict__ r, int N, int D, float* __restrict__ dres,
+    T* __restrict__ dres_t) {
+    constexpr int V = Elt<T>::kVec;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= N) return;
+    const T* g = dn + row * D;
+    const T* xr = x + row * D;
+    uint4 xraw[MAXC], graw[MAXC];
+    float dot = 0.f;
+#pragma unroll
+    for (int ci = 0; ci < MAXC; ++ci) {
+        const int c = (ci * kWave + lane) * V;
+        if (c < D) {
+            xraw[ci] = *reinterpret_cast<const uint4*>(xr + c);
+            graw[ci] = *reinterpret_cast<const uint4*>(g + c);
+            float xv[V], gv[V];
+            unpack_chunk<T>(xraw[ci], xv);
+            unpack_chunk<T>(graw[ci], gv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) dot += gv[k] * xv[k];
+        }
+    }
+    dot = wave_sum(dot);
+    const float rr = r[row];
+    const float coef = rr * rr * dot / (float)D;
+    float* d = dres + row * D;
+    T* dt = dres_t + row * D;
+#pragma unroll
+    for (int ci = 0; ci < MAXC; ++ci) {
+        const int c = (ci * kWave + lane) * V;
+        if (c < D) {
+            float xv[V], gv[V], o[V];
+            unpack_chunk<T>(xraw[ci], xv);
+            unpack_chunk<T>(graw[ci], gv);
+#pragma unroll
+            for (int k = 0; k < V; ++k) o[k] = d[c + k] + gv[k] - coef * xv[k];
+#pragma unroll
+            for (int k = 0; k < V; ++k) d[c + k] = o[k];
+            st_vec<T>(dt + c, o);
+        }
+    }
 }
 
 template <typename T, int MAXC>
@@ -474,9 +488,21 @@ hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk, const
 template <typename T>
 hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D,
                           float* dres, T* dres_t, hipStream_t s) {
-    hipLaunchKernelGGL(k_norm_bwd_resid<T>, dim3(row_blocks(N)), dim3(kRowThreads), 0, s, dn, x,
-                       r, N, D, dres, dres_t);
-    return hipGetLastError();
+    constexpr int VEC = Elt<T>::kVec;
+    const int chunks = (int)ceil_div(D, kWave * VEC);
+#define NC_NB_CASE(C)                                                                         \
+    if (chunks <= C) {                                                                        \
+        hipLaunchKernelGGL((k_norm_bwd_resid<T, C>), dim3(row_blocks(N)), dim3(kRowThreads), 0, \
+                           s, dn, x, r, N, D, dres, dres_t);                                  \
+        return hipGetLastError();                                                             \
+    }
+    NC_NB_CASE(1)
+    NC_NB_CASE(2)
+    NC_NB_CASE(4)
+    NC_NB_CASE(8)
+    NC_NB_CASE(16)
+#undef NC_NB_CASE
+    return hipErrorInvalidValue;   // rows longer than 16 chunks per lane
 }
 
 template <typename T>

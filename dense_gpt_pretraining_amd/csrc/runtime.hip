@@ -50,9 +50,12 @@ int validate(const nc_config* c) {
     if (c->seq_len % 64) return NC_ERR_UNSUPPORTED;
     if (c->softcap > 60.f) return NC_ERR_UNSUPPORTED;
     if (c->vocab > (1 << 24)) return NC_ERR_UNSUPPORTED;
-    // the fused cross-entropy keeps a padded vocabulary row in registers
-    const int64_t row_cap = (int64_t)32 * 256 * (c->dtype == NC_BF16 ? 8 : 4);
-    if (vocab_pad(*c) > row_cap) return NC_ERR_UNSUPPORTED;
+    // the fused cross-entropy keeps a padded vocabulary row in registers (32
+    // 16-byte chunks per thread of 512), and the norm backward a residual row
+    // (16 chunks per lane of 64)
+    const int64_t vec = c->dtype == NC_BF16 ? 8 : 4;
+    if (vocab_pad(*c) > 32 * 512 * vec) return NC_ERR_UNSUPPORTED;
+    if (c->d_model > 16 * 64 * vec) return NC_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)c->batch * c->seq_len;
     if (N > (1 << 24)) return NC_ERR_UNSUPPORTED;
     const int64_t widest = std::max<int64_t>(

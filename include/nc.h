@@ -59,12 +59,14 @@ enum {
 /*
  * Model and batch description.
  *   n_layer    number of blocks (>= 1)
- *   d_model    width D of the residual stream (multiple of 64)
+ *   d_model    width D of the residual stream (multiple of 64; at most 8192
+ *              for NC_BF16, 4096 for NC_F32)
  *   n_head     H, query heads; n_head * head_dim is the attention width
  *   head_dim   hd, 64 or 128
  *   n_kv_head  must be 1: multi-query attention (one K head, one V head)
  *   d_mlp      F, hidden width of the relu^2 MLP (multiple of 64)
- *   vocab      V >= 2
+ *   vocab      V >= 2 (padded to a multiple of 256: at most 131072 for NC_BF16,
+ *              65536 for NC_F32)
  *   seq_len    T, a multiple of 64
  *   batch      B >= 1 sequences; tokens per step N = B*T
  *   rope_base  rotary base (angle of pair i at position t: t*base^(-2i/hd))
