@@ -16,13 +16,16 @@
 //   (buffer loads with the LDS bit, no staging registers); the loads of tile k+1
 //   are in flight while tile k is multiplied.
 //   k-major tiles are stored 256 rows x 64 k and a fragment is one 16-byte
-//   read; the fragments of k step s+1 are read while the matrix instructions
-//   of step s issue.  mn-major tiles (the weight-gradient layout) are stored
-//   as they lie in memory, 64 k x 256 rows, and a fragment (8 consecutive k
-//   of one row) is two LDS transpose reads (ds_read_b64_tr_b16), so no layout
-//   is ever transposed in registers; all of a tile's transpose reads are
-//   issued before the next tile's copy (the compiler would otherwise wait for
-//   the copy before each of them).
+//   read.  mn-major tiles (the weight-gradient layout) are stored as they lie
+//   in memory, 64 k x 256 rows, and a fragment (8 consecutive k of one row)
+//   is two LDS transpose reads (ds_read_b64_tr_b16), so no layout is ever
+//   transposed in registers.  In both, the fragments of k step s+1 are read
+//   while the matrix instructions of step s issue.  The buffers are four
+//   distinct LDS arrays, the k loop is unrolled by two so that each access
+//   names its array at compile time, and every access is one byte offset from
+//   its array: only then can the compiler tell that LDS reads of one buffer do
+//   not alias copies in flight into the other (otherwise it waits for those
+//   copies before the reads).
 // The MFMA "A" side takes the n rows and the "B" side the m rows, which puts
 // 4 consecutive n of one row m in each lane's accumulator registers: the
 // epilogue stores 8 (bf16) or 16 (fp32) contiguous bytes per lane.
@@ -458,10 +461,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                                                            const bf16_t* __restrict__ B,
                                                            int64_t ldb, void* C, int64_t ldc,
                                                            EpiDev e, int64_t split_stride) {
-    // two distinct buffers (A tile then B tile each), so the compiler can see
-    // that loads into one never alias reads of the other
-    __shared__ __align__(16) bf16_t lds0[2 * kTileElems];
-    __shared__ __align__(16) bf16_t lds1[2 * kTileElems];
+    // two buffers of an A tile and a B tile, as four distinct arrays: with the
+    // buffer known at compile time (the k loop is unrolled by two) and one
+    // byte offset from the array's start per access, the compiler can see
+    // that copies into one buffer never alias reads of the other
+    __shared__ __align__(16) bf16_t ldsA0[kTileElems];
+    __shared__ __align__(16) bf16_t ldsA1[kTileElems];
+    __shared__ __align__(16) bf16_t ldsB0[kTileElems];
+    __shared__ __align__(16) bf16_t ldsB1[kTileElems];
 
     const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     const int total = tiles_m * tiles_n;
@@ -524,12 +531,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) trb[i] = mn_frag_off(wn * 128 + i * 32, lane);
     const int nk = (ke - kb + kTK - 1) / kTK;
-    auto issue = [&](int kt, bf16_t* buf) {
+    auto issue = [&](int kt, bf16_t* ta, bf16_t* tb) {
         const int k0 = kb + kt * kTK;
-        if (AK) kmaj_issue(A + (int64_t)m0 * lda + k0, la, buf, wave);
-        else mn_issue(A + (int64_t)k0 * lda + m0, ma, buf, wave);
-        if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, buf + kTileElems, wave);
-        else mn_issue(B + (int64_t)k0 * ldb + n0, mb, buf + kTileElems, wave);
+        if (AK) kmaj_issue(A + (int64_t)m0 * lda + k0, la, ta, wave);
+        else mn_issue(A + (int64_t)k0 * lda + m0, ma, ta, wave);
+        if (BK) kmaj_issue(B + (int64_t)n0 * ldb + k0, lb, tb, wave);
+        else mn_issue(B + (int64_t)k0 * ldb + n0, mb, tb, wave);
     };
     // the epilogue's aux rows (x of the residual, g of the relu^2 backward)
     constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
@@ -548,100 +555,71 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         }
     };
     if (nk > 0) {
-        issue(0, lds0);
+        issue(0, ldsA0, ldsB0);
         wait_vmem();
     }
     __syncthreads();
     {
-        // fragments of k step ks+1 (or of the next tile's first step) are
-        // read while the 8 matrix instructions of step ks issue
+        // fragments of k step ks+1 are read while the 8 matrix instructions
+        // of step ks issue
         const int rowoff = (lane & 31) * kTK;
         bf16x8_t fa[2][4], fb[2][2];
-        auto rd_a = [&](const bf16_t* sB, int ks, int set, int i) {
-            fa[set][i] = BK ? as_bf16x8(*reinterpret_cast<const uint4*>(
-                                  sB + (wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]))
-                            : mn_frag(reinterpret_cast<const char*>(sB) + trb[i] + ks * 16 * 512);
+        auto ld16 = [](const bf16_t* t, int byte_off) {
+            return as_bf16x8(*reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(t) +
+                                                             byte_off));
         };
-        auto rd_b = [&](const bf16_t* sA, int ks, int set, int j) {
-            fb[set][j] = AK ? as_bf16x8(*reinterpret_cast<const uint4*>(
-                                  sA + (wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]))
-                            : mn_frag(reinterpret_cast<const char*>(sA) + tra[j] + ks * 16 * 512);
+        auto rd_a = [&](const bf16_t* tb, int ks, int set, int i) {
+            fa[set][i] = BK ? ld16(tb, 2 * ((wn * 128 + i * 32) * kTK + rowoff + foff[i & 1][ks]))
+                            : mn_frag(reinterpret_cast<const char*>(tb) + (trb[i] + ks * 16 * 512));
+        };
+        auto rd_b = [&](const bf16_t* ta, int ks, int set, int j) {
+            fb[set][j] = AK ? ld16(ta, 2 * ((wm * 64 + j * 32) * kTK + rowoff + foff[j & 1][ks]))
+                            : mn_frag(reinterpret_cast<const char*>(ta) + (tra[j] + ks * 16 * 512));
         };
         // a step's fragments are read in the order its products first use
         // them (block i outer, j inner), so its first products wait for the
         // first two reads only
-        auto rd = [&](const bf16_t* buf, int ks, int set) {
-            const bf16_t* sA = buf;
-            const bf16_t* sB = buf + kTileElems;
-            rd_a(sB, ks, set, 0);
-            rd_b(sA, ks, set, 0);
-            rd_b(sA, ks, set, 1);
-            rd_a(sB, ks, set, 1);
-            rd_a(sB, ks, set, 2);
-            rd_a(sB, ks, set, 3);
+        auto rd = [&](const bf16_t* ta, const bf16_t* tb, int ks, int set) {
+            rd_a(tb, ks, set, 0);
+            rd_b(ta, ks, set, 0);
+            rd_b(ta, ks, set, 1);
+            rd_a(tb, ks, set, 1);
+            rd_a(tb, ks, set, 2);
+            rd_a(tb, ks, set, 3);
         };
-        for (int kt = 0; kt < nk; ++kt) {
-            bf16_t* cur = (kt & 1) ? lds1 : lds0;
-            bf16_t* nxt = (kt & 1) ? lds0 : lds1;
+        // one k tile from (ca, cb); the next one is copied into (na, nb)
+        auto step = [&](int kt, const bf16_t* ca, const bf16_t* cb, bf16_t* na, bf16_t* nb) {
             if (kt > 0) {
                 // tile kt has landed (this wave's loads) and every wave is
                 // done reading tile kt-1, whose buffer is refilled next
                 wait_vmem();
                 barrier_nofence();
             }
-            if constexpr (!AK) {
-                // mn-major: every transpose read of the tile is issued before
-                // the next tile's copy.  (The compiler cannot tell that a
-                // transpose read does not alias an LDS copy in flight and
-                // would wait for the copy before each one.)
-                bf16x8_t ga[kTK / 16][4], gb[kTK / 16][2];
-                const char* sA = reinterpret_cast<const char*>(cur);
-                const char* sB = reinterpret_cast<const char*>(cur + kTileElems);
-#pragma unroll
-                for (int ks = 0; ks < kTK / 16; ++ks) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ga[ks][i] = mn_frag(sB + trb[i] + ks * 16 * 512);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) gb[ks][j] = mn_frag(sA + tra[j] + ks * 16 * 512);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (kt + 1 < nk) issue(kt + 1, nxt);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ks = 0; ks < kTK / 16; ++ks)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = mfma32(ga[ks][i], gb[ks][j], acc[i][j]);
-                continue;
-            }
             if (kt == 0) {
                 // first tile: its first fragments are read before the next
-                // tile's copy is issued (the compiler would wait for that copy
-                // before the reads)
-                rd(cur, 0, 0);
-                if (kt + 1 < nk) issue(kt + 1, nxt);
+                // tile's copy is issued
+                rd(ca, cb, 0, 0);
+                if (kt + 1 < nk) issue(kt + 1, na, nb);
             } else {
-                if (kt + 1 < nk) issue(kt + 1, nxt);
-                rd(cur, 0, 0);
+                if (kt + 1 < nk) issue(kt + 1, na, nb);
+                rd(ca, cb, 0, 0);
             }
 #pragma unroll
             for (int ks = 0; ks < kTK / 16; ++ks) {
                 const int cs = ks & 1;
-                if (ks + 1 < kTK / 16) rd(cur, ks + 1, cs ^ 1);
+                if (ks + 1 < kTK / 16) rd(ca, cb, ks + 1, cs ^ 1);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
                 // interleave the next step's fragment reads with this step's
-                // products: 2 MFMAs, 2 reads, ... (the fastest of the
-                // patterns tried over the whole step)
+                // products: k-major 2 MFMAs / 2 reads, mn-major (two
+                // transpose reads per fragment) 1 MFMA / 3 reads
                 if (ks + 1 < kTK / 16) {
-                    constexpr int kGroups = 3;
-                    constexpr int kMfmaPerGroup = 2;
-                    constexpr int kReadsPerGroup = 2;
+                    constexpr int kGroups = AK ? 3 : 4;
+                    constexpr int kMfmaPerGroup = AK ? 2 : 1;
+                    constexpr int kReadsPerGroup = AK ? 2 : 3;
 #pragma unroll
                     for (int x = 0; x < kGroups; ++x) {
                         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerGroup, 0);   // MFMA
@@ -652,6 +630,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, ldsA0, ldsB0, ldsA1, ldsB1);
+            if (kt + 1 < nk) step(kt + 1, ldsA1, ldsB1, ldsA0, ldsB0);
         }
     }
 
@@ -663,7 +645,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     // back two rows per instruction: lane l takes row 2 t + (l >> 5), columns
     // 4 (l & 31) .. +3, so 32 lanes cover one row's 128 columns contiguously.
     __syncthreads();   // every wave is done with the last k tile
-    float* stage = reinterpret_cast<float*>(wave < 4 ? lds0 : lds1) + (wave & 3) * 4096;
+    // (two waves' 16 KB per 32 KB array)
+    bf16_t* const stage_arr = wave < 2 ? ldsA0 : wave < 4 ? ldsA1 : wave < 6 ? ldsB0 : ldsB1;
+    float* stage = reinterpret_cast<float*>(stage_arr) + (wave & 1) * 4096;
     constexpr bool kRs = MODE == EPI_ROWSCALE || MODE == EPI_ROWSCALE_RELU2 || MODE == EPI_RELU2_BWD;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
