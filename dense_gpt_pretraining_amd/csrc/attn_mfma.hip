@@ -136,15 +136,15 @@ __device__ __forceinline__ void tile_lane_offsets(int w, int lane, int64_t ld, i
 }
 
 // copy one K tile and one V tile (rows kb.. of the sequence, byte offset
-// `base`) into LDS at sK and sK + tb: this wave's NI instructions of each
+// `base`) into LDS at sK and sV: this wave's NI instructions of each
 template <int NI>
 __device__ __forceinline__ void copy_kv_tile(const char* kg, const char* vg, int64_t base,
-                                             const int (&ld_src)[NI], char* sK, int tb, int w) {
+                                             const int (&ld_src)[NI], char* sK, char* sV, int w) {
     const buf_rsrc_t rk = make_rsrc(kg + base), rv = make_rsrc(vg + base);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         lds_copy<16>(rk, ld_src[i], sK + (w * NI + i) * 1024);
-        lds_copy<16>(rv, ld_src[i], sK + tb + (w * NI + i) * 1024);
+        lds_copy<16>(rv, ld_src[i], sV + (w * NI + i) * 1024);
     }
 }
 
@@ -155,7 +155,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     int64_t ldq, int64_t ldkv, bf16_t* __restrict__ o, float* __restrict__ lse, int B, int T,
     int H, float scale_log2) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
-    __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
+    // two buffers of a K tile and a V tile, as four distinct arrays: with the
+    // buffer known at compile time (the key loop is unrolled by two) and one
+    // byte offset from the array per access, the compiler can see that reads
+    // of one buffer never alias the copies in flight into the other
+    __shared__ __align__(1024) char sK0[TB];
+    __shared__ __align__(1024) char sV0[TB];
+    __shared__ __align__(1024) char sK1[TB];
+    __shared__ __align__(1024) char sV1[TB];
 
     const int rows_total = T * H;
     const int n_rb = (rows_total + kRB - 1) / kRB;
@@ -189,8 +196,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     tile_lane_offsets<HD, NI>(w, lane, ldkv, ld_src, row_off, tr_off);
     const char* kg = reinterpret_cast<const char*>(k + seq0 * ldkv);
     const char* vg = reinterpret_cast<const char*>(v + seq0 * ldkv);
-    auto issue = [&](int kb, int buf) {
-        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, sm + buf * 2 * TB, TB, w);
+    auto issue = [&](int kb, char* dk, char* dv) {
+        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, dk, dv, w);
     };
 
     f32x16_t oacc[HD / 32];
@@ -198,21 +205,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     for (int db = 0; db < HD / 32; ++db) oacc[db] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
 
-    issue(0, 0);
-    for (int it = 0; it < n_tiles; ++it) {
+    issue(0, sK0, sV0);
+    // key tile it from (sK, sV); the next one is copied into (nK, nV)
+    auto tile = [&](int it, const char* sK, const char* sV, char* nK, char* nV) {
         const int kb = it * kKT;
         wait_vmem();
         barrier_nofence();
-        if (it + 1 < n_tiles) issue(kb + kKT, (it + 1) & 1);
-        const char* sK = sm + (it & 1) * 2 * TB;
-        const char* sV = sK + TB;
-        if (kb > tw_max) continue;
+        if (it + 1 < n_tiles) issue(kb + kKT, nK, nV);
+        if (kb > tw_max) return;
         f32x16_t s[2] = {zero16(), zero16()};
 #pragma unroll
         for (int kk = 0; kk < HD / 16; ++kk)
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-                s[bi] = mfma32(lds_b128(sK + bi * 32 * HD * 2 + row_off[kk]), qf[kk], s[bi]);
+                s[bi] = mfma32(lds_b128(sK + (bi * 32 * HD * 2 + row_off[kk])), qf[kk], s[bi]);
         // keys beyond a row's position exist only on tiles that reach past
         // the wave's first position
         if (kb + kKT - 1 > tw_min) {
@@ -256,12 +262,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 #pragma unroll
             for (int e = 0; e < 8; ++e) pv[e] = s[bi][8 * h + e];
             const bf16x8_t bp = pack8(pv);
-            const char* vb = sV + (32 * bi + 16 * h) * HD * 2;
+            const int vb = (32 * bi + 16 * h) * HD * 2;
 #pragma unroll
             for (int db = 0; db < HD / 32; ++db)
-                oacc[db] = mfma32(lds_tr_frag(vb + tr_off[db][0], vb + tr_off[db][1]), bp,
-                                  oacc[db]);
+                oacc[db] = mfma32(lds_tr_frag(sV + (vb + tr_off[db][0]), sV + (vb + tr_off[db][1])),
+                                  bp, oacc[db]);
         }
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile(it, sK0, sV0, sK1, sV1);
+        if (it + 1 < n_tiles) tile(it + 1, sK1, sV1, sK0, sV0);
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -289,7 +299,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq, int B,
     int T, int H, float scale_log2, float scale, AttnBwdFuse fz) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
-    __shared__ __align__(1024) char sm[2 * 2 * TB];   // [buffer][K | V]
+    // two buffers of a K and a V tile as four distinct arrays (see the
+    // forward kernel)
+    __shared__ __align__(1024) char sK0[TB];
+    __shared__ __align__(1024) char sV0[TB];
+    __shared__ __align__(1024) char sK1[TB];
+    __shared__ __align__(1024) char sV1[TB];
 
     const int rows_total = T * H;
     const int n_rb = (rows_total + kRB - 1) / kRB;
@@ -346,33 +361,31 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     tile_lane_offsets<HD, NI>(w, lane, ldkv, ld_src, row_off, tr_off);
     const char* kg = reinterpret_cast<const char*>(k + seq0 * ldkv);
     const char* vg = reinterpret_cast<const char*>(v + seq0 * ldkv);
-    auto issue = [&](int kb, int buf) {
-        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, sm + buf * 2 * TB, TB, w);
+    auto issue = [&](int kb, char* dk, char* dv) {
+        copy_kv_tile<NI>(kg, vg, (int64_t)kb * ldkv * 2, ld_src, dk, dv, w);
     };
 
     f32x16_t acc[HD / 32];
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) acc[db] = zero16();
 
-    issue(0, 0);
-    for (int it = 0; it < n_tiles; ++it) {
+    issue(0, sK0, sV0);
+    // key tile it from (sK, sV); the next one is copied into (nK, nV)
+    auto tile = [&](int it, const char* sK, const char* sV, char* nK, char* nV) {
         const int kb = it * kKT;
         wait_vmem();
         barrier_nofence();
-        if (it + 1 < n_tiles) issue(kb + kKT, (it + 1) & 1);
-        const char* sK = sm + (it & 1) * 2 * TB;
-        const char* sV = sK + TB;
-        if (kb > tw_max) continue;
+        if (it + 1 < n_tiles) issue(kb + kKT, nK, nV);
+        if (kb > tw_max) return;
         const bool diag = kb + kKT - 1 > tw_min;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
             f32x16_t s = zero16(), dp = zero16();
-            const char* kr = sK + bi * 32 * HD * 2;
-            const char* vr = sV + bi * 32 * HD * 2;
+            const int rb0 = bi * 32 * HD * 2;
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
-                s = mfma32(lds_b128(kr + row_off[kk]), qf[kk], s);
-                dp = mfma32(lds_b128(vr + row_off[kk]), df[kk], dp);
+                s = mfma32(lds_b128(sK + (rb0 + row_off[kk])), qf[kk], s);
+                dp = mfma32(lds_b128(sV + (rb0 + row_off[kk])), df[kk], dp);
             }
             float ds[16];
 #pragma unroll
@@ -387,13 +400,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bf16x8_t bd = pack8(&ds[8 * h]);
-                const char* kt = kr + 16 * h * HD * 2;
+                const int kt = rb0 + 16 * h * HD * 2;
 #pragma unroll
                 for (int db = 0; db < HD / 32; ++db)
-                    acc[db] = mfma32(lds_tr_frag(kt + tr_off[db][0], kt + tr_off[db][1]),
+                    acc[db] = mfma32(lds_tr_frag(sK + (kt + tr_off[db][0]), sK + (kt + tr_off[db][1])),
                                      bd, acc[db]);
             }
         }
+    };
+    for (int it = 0; it < n_tiles; it += 2) {
+        tile(it, sK0, sV0, sK1, sV1);
+        if (it + 1 < n_tiles) tile(it + 1, sK1, sV1, sK0, sV0);
     }
     if (!valid) return;
     if constexpr (!FUSE) {
