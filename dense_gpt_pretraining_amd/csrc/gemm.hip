@@ -614,12 +614,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     for (int j = 0; j < 2; ++j)
                         acc[i][j] = mfma32(fa[cs][i], fb[cs][j], acc[i][j]);
                 // interleave the next step's fragment reads with this step's
-                // products: k-major 2 MFMAs / 2 reads, mn-major (two
-                // transpose reads per fragment) 1 MFMA / 3 reads
+                // products: k-major 2 MFMAs / 2 reads, with an mn-major operand
+                // (two transpose reads per fragment) 1 MFMA / 3 reads
                 if (ks + 1 < kTK / 16) {
-                    constexpr int kGroups = AK ? 3 : 4;
-                    constexpr int kMfmaPerGroup = AK ? 2 : 1;
-                    constexpr int kReadsPerGroup = AK ? 2 : 3;
+                    constexpr bool kKm = AK && BK;
+                    constexpr int kGroups = kKm ? 3 : 4;
+                    constexpr int kMfmaPerGroup = kKm ? 2 : 1;
+                    constexpr int kReadsPerGroup = kKm ? 2 : 3;
 #pragma unroll
                     for (int x = 0; x < kGroups; ++x) {
                         __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerGroup, 0);   // MFMA
@@ -821,6 +822,11 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
         }
     } else if (!a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
         err = launch_mfma<false, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+    } else if (a_kmajor && !b_kmajor && epi.mode == EPI_STORE_T) {
+        // data gradients dX = dY W straight from the [out][in] weight
+        err = launch_mfma<true, false, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+    } else if (a_kmajor && !b_kmajor && epi.mode == EPI_RELU2_BWD) {
+        err = launch_mfma<true, false, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
     } else {
         return hipErrorInvalidValue;  // layout/epilogue pair the step never uses
     }

@@ -110,6 +110,14 @@ struct Plan {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// data-gradient product C = A W (M x N, contraction K) with the [K][N] weight
+// read where it is stored, as an mn-major operand: no transposed copy
+template <typename T>
+hipError_t gemm_w(int M, int N, int K, const T* A, int64_t lda, const T* W, int64_t ldw, T* C,
+                  int64_t ldc, const nc::Epilogue& e, hipStream_t s) {
+    return nc::gemm<T>(M, N, K, A, lda, true, W, ldw, false, C, ldc, e, nullptr, 0, s);
+}
+
 Plan make_plan(const nc_config& c, bool bwd) {
     Plan p;
     const int64_t N = (int64_t)c.batch * c.seq_len;
@@ -408,30 +416,24 @@ struct Step {
             T* x = X(l);
             T* xm = XM(l);
             // MLP: x_{l+1} = xm + relu(r2 xm W_fc^T)^2 W_proj^T
-            NC_RUN("transpose_w", 0, tb(D, F),
-                   nc::transpose<T>(W(i_layer(l, 5)), (int)D, (int)F, F, wt, D, s));
             NC_RUN("gemm_nt_relu2_bwd", gf(N, F, D), gb(N, F, D, es(), N * F * es() + N * 4.0),
-                   nc::gemm<T>((int)N, (int)F, (int)D, dres_t, D, true, wt, D, true, dgu, F,
-                               epi(nc::EPI_RELU2_BWD, R2(l), G(l)), nullptr, 0, s));
+                   gemm_w<T>((int)N, (int)F, (int)D, dres_t, D, W(i_layer(l, 5)), F, dgu, F,
+                             epi(nc::EPI_RELU2_BWD, R2(l), G(l)), s));
             NC_RUN("gemm_tn_f32", gf(D, F, N), gb(D, F, N, 4.0),
                    nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(l), F, false,
                                G_of(i_layer(l, 5)), F, epi(nc::EPI_STORE_F32), sk, skb, s));
-            NC_RUN("transpose_w", 0, tb(F, D),
-                   nc::transpose<T>(W(i_layer(l, 4)), (int)F, (int)D, D, wt, F, s));
             NC_RUN("gemm_nt_dn", gf(N, D, F), gb(N, D, F, es()),
-                   nc::gemm<T>((int)N, (int)D, (int)F, dgu, F, true, wt, F, true, dn, D,
-                               epi(nc::EPI_STORE_T), nullptr, 0, s));
+                   gemm_w<T>((int)N, (int)D, (int)F, dgu, F, W(i_layer(l, 4)), D, dn, D,
+                             epi(nc::EPI_STORE_T), s));
             NC_RUN("gemm_tn_f32", gf(F, D, N), gb(F, D, N, 4.0),
                    nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
                                G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("norm_bwd_resid", 0, nbb,
                    nc::norm_bwd_resid<T>(dn, xm, R2(l), (int)N, (int)D, dres, dres_t, s));
             // attention: xm = x + o W_o^T
-            NC_RUN("transpose_w", 0, tb(D, H * hd),
-                   nc::transpose<T>(W(i_layer(l, 3)), (int)D, (int)(H * hd), H * hd, wt, D, s));
             NC_RUN("gemm_nt_store", gf(N, H * hd, D), gb(N, H * hd, D, es()),
-                   nc::gemm<T>((int)N, (int)(H * hd), (int)D, dres_t, D, true, wt, D, true, dout,
-                               H * hd, epi(nc::EPI_STORE_T), nullptr, 0, s));
+                   gemm_w<T>((int)N, (int)(H * hd), (int)D, dres_t, D, W(i_layer(l, 3)), H * hd,
+                             dout, H * hd, epi(nc::EPI_STORE_T), s));
             NC_RUN("gemm_tn_f32", gf(D, H * hd, N), gb(D, H * hd, N, 4.0),
                    nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(l), H * hd,
                                false, G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb,
@@ -469,11 +471,9 @@ struct Step {
                        nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
                                               (int)H, (int)hd, cos_t, sin_t, dqkv, s));
             }
-            NC_RUN("transpose_w", 0, tb(Wq, D),
-                   nc::transpose<T>(W(i_layer(l, 0)), (int)Wq, (int)D, D, wt, Wq, s));
             NC_RUN("gemm_nt_dn", gf(N, D, Wq), gb(N, D, Wq, es()),
-                   nc::gemm<T>((int)N, (int)D, (int)Wq, dqkv, Wq, true, wt, Wq, true, dn, D,
-                               epi(nc::EPI_STORE_T), nullptr, 0, s));
+                   gemm_w<T>((int)N, (int)D, (int)Wq, dqkv, Wq, W(i_layer(l, 0)), D, dn, D,
+                             epi(nc::EPI_STORE_T), s));
             NC_RUN("gemm_tn_f32", gf(Wq, D, N), gb(Wq, D, N, 4.0),
                    nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
                                G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
