@@ -237,6 +237,8 @@ __device__ __forceinline__ bf16x8_t mn_frag(const char* p) {
 
 // wait until this thread's direct global->LDS loads have landed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// wait until this thread's LDS reads and writes have completed
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // workgroup barrier without the memory fence __syncthreads() implies: the
 // fence would wait for every outstanding load, including the direct loads of
@@ -645,7 +647,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     // LDS (16-byte chunk c of row r at chunk position c ^ r), then reads it
     // back two rows per instruction: lane l takes row 2 t + (l >> 5), columns
     // 4 (l & 31) .. +3, so 32 lanes cover one row's 128 columns contiguously.
-    __syncthreads();   // every wave is done with the last k tile
+    // Every wave is done reading the last k tile.  From here on each wave
+    // works in its own slot of LDS, so the passes need no workgroup barrier
+    // (a wave's LDS accesses are performed in order) and no fence, which would
+    // wait for the previous pass's output stores.
+    wait_lds();
+    barrier_nofence();
     // (two waves' 16 KB per 32 KB array)
     bf16_t* const stage_arr = wave < 2 ? ldsA0 : wave < 4 ? ldsA1 : wave < 6 ? ldsB0 : ldsB1;
     float* stage = reinterpret_cast<float*>(stage_arr) + (wave & 1) * 4096;
@@ -671,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                 acc[i][j][4 * q + 3]);
             }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
         const int64_t n = n0 + wn * 128 + 4 * li;
         if (MODE == EPI_QKV_ROPE && e.head_dim == 128) {
             qkv_rope_pass128(e, static_cast<bf16_t*>(C), ldc, M, N, stage, m0 + wm * 64 + 32 * j,
@@ -696,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                     if (n + q < N) epi_store1<bf16_t>(e, C, ldc, m, n + q, a[q]);
             }
         }
-        if (j == 0) __syncthreads();
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
