@@ -719,6 +719,27 @@ __global__ void k_splitk_reduce(const float* __restrict__ part, int splits, int 
     out[m * ldc + n] = s;
 }
 
+// the same, four consecutive n per thread (N, ldc, ldp multiples of 4 and
+// 16-byte aligned rows); each element is summed in the same order
+__global__ void k_splitk_reduce4(const float* __restrict__ part, int splits, int M, int N4,
+                                 int64_t ldp, float* __restrict__ out, int64_t ldc,
+                                 int accumulate) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)M * N4) return;
+    const int64_t m = i / N4, n = (i - m * N4) * 4;
+    float4 acc = accumulate ? *reinterpret_cast<const float4*>(out + m * ldc + n)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int p = 0; p < splits; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)p * M + m) * ldp + n);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + m * ldc + n) = acc;
+}
+
 // k-split of a GEMM with few output tiles: the split count s that minimises
 // the modelled time rounds(s) * (k per split + c), rounds(s) = workgroup
 // waves of tiles * s over the 256 compute units and c ~ the fixed cost of a
@@ -841,9 +862,16 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
     const int64_t n = (int64_t)M * N;
     err = prof_cut("splitk_reduce", 0, 4.0 * n * (splits + 1 + e.accumulate));
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
-                       splitk_ws, splits, M, N, splitk_ld(N), static_cast<float*>(C), ldc,
-                       e.accumulate);
+    if (N % 4 == 0 && reinterpret_cast<uintptr_t>(C) % 16 == 0) {
+        const int64_t n4 = n / 4;
+        hipLaunchKernelGGL(k_splitk_reduce4, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s,
+                           splitk_ws, splits, M, N / 4, splitk_ld(N), static_cast<float*>(C),
+                           ldc, e.accumulate);
+    } else {
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s,
+                           splitk_ws, splits, M, N, splitk_ld(N), static_cast<float*>(C), ldc,
+                           e.accumulate);
+    }
     return hipGetLastError();
 }
 
