@@ -145,10 +145,6 @@ constexpr int kTM = 256, kTN = 256, kTK = 64;
 constexpr int kThreads = 512;                         // 8 waves, 2 per SIMD
 constexpr int kTileElems = kTM * kTK;                 // one operand tile (256 rows x 64 k)
 
-// element offset of 16-byte chunk `ch` (0..7) of row `row` in a swizzled tile
-__device__ __forceinline__ int swz_f(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int swz(int row, int ch) { return row * kTK + ((ch ^ swz_f(row)) << 3); }
-
 // Stage one 256-row x 64-k operand tile into LDS.
 //   k-major: straight from global memory into LDS (buffer load, LDS bit).
 //     Wave w's instruction i fills the 64 consecutive 16-byte LDS slots of
@@ -344,7 +340,7 @@ __device__ __forceinline__ void epi_vec4_pre(const EpiDev& e, void* C, int64_t i
 // with i + hd/2, which sits hd/8 lanes away -- and RMS-normalised over its
 // group; the value head is stored as u.
 __device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
-                                               int N, int64_t m, int64_t n, int li, float4 v) {
+                                               int N, int64_t m, int64_t n, float4 v) {
     // 32-bit index arithmetic (rows < 2^24, columns < 2^16); head_dim is a
     // power of two
     const int hd = e.head_dim, half = hd >> 1, H = e.n_head;
@@ -691,7 +687,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             const int64_t m = m0 + wm * 64 + 32 * j + row;
             if (MODE == EPI_QKV_ROPE) {
                 // every lane of the half-wave joins the head's shuffles
-                qkv_rope_store(e, static_cast<bf16_t*>(C), ldc, M, N, m, n, li, v);
+                qkv_rope_store(e, static_cast<bf16_t*>(C), ldc, M, N, m, n, v);
                 continue;
             }
             if (m >= M) continue;

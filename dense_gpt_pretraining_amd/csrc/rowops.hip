@@ -348,7 +348,7 @@ __global__ __launch_bounds__(1024) void k_mean_reduce(const float* __restrict__ 
     red[threadIdx.x] = s;
     __syncthreads();
     for (int w = 512; w > 0; w >>= 1) {
-        if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
         __syncthreads();
     }
     if (threadIdx.x == 0) out[0] = (float)(red[0] / (double)N);
