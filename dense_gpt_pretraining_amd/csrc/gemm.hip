@@ -846,6 +846,8 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
         }
     } else if (!a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
         err = launch_mfma<false, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+    } else if (a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
+        err = launch_mfma<true, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
     } else if (a_kmajor && !b_kmajor && epi.mode == EPI_STORE_T) {
         // data gradients dX = dY W straight from the [out][in] weight
         err = launch_mfma<true, false, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);

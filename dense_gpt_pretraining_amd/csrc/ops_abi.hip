@@ -35,10 +35,11 @@ int nc_op_matmul(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
         return ret(nc::gemm<float>(M, N, K, static_cast<const float*>(A), lda, a_kmajor != 0,
                                    static_cast<const float*>(B), ldb, b_kmajor != 0, C, ldc, e,
                                    static_cast<float*>(ws), ws_bytes, s));
-    if ((a_kmajor != 0) != (b_kmajor != 0)) return NC_ERR_UNSUPPORTED;
+    if (!a_kmajor && b_kmajor) return NC_ERR_UNSUPPORTED;   // (mn-major, k-major) is not built
     if (K % 8 || lda % 8 || ldb % 8 || ldc % 4) return NC_ERR_UNSUPPORTED;
     if (K % 64) return NC_ERR_UNSUPPORTED;   // whole 64-deep k tiles are copied into LDS
-    if (!a_kmajor && (lda < ((M + 7) / 8) * 8 || ldb < ((N + 7) / 8) * 8)) return NC_ERR_UNSUPPORTED;
+    if (!a_kmajor && lda < ((M + 7) / 8) * 8) return NC_ERR_UNSUPPORTED;
+    if (!b_kmajor && ldb < ((N + 7) / 8) * 8) return NC_ERR_UNSUPPORTED;
     return ret(nc::gemm<nc::bf16_t>(M, N, K, static_cast<const nc::bf16_t*>(A), lda,
                                     a_kmajor != 0, static_cast<const nc::bf16_t*>(B), ldb,
                                     b_kmajor != 0, C, ldc, e, static_cast<float*>(ws), ws_bytes,

@@ -24,7 +24,8 @@ extern "C" {
  * ldc.  A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m] (T), likewise B with
  * b_kmajor.  This is the contraction of every bias-free linear layer (forward
  * X W^T, data gradient dY W, weight gradient dY^T X).  bf16 supports the
- * (k-major, k-major) and (mn-major, mn-major) pairs with K a multiple of 64;
+ * (k-major, k-major), (k-major, mn-major) and (mn-major, mn-major) pairs with
+ * K a multiple of 64;
  * both leading dimensions must be multiples of 8 (for mn-major operands at
  * least M resp. N rounded up to 8) and ldc a multiple of 4.  ws (may be NULL, ws_bytes 0) is scratch
  * for a k-split; with too little scratch the k loop is not split.

@@ -119,6 +119,10 @@ def test_status_strings():
 
 def test_ops_validation():
     b = _b()
+    # bf16 (mn-major A, k-major B) is not built; K must be a multiple of 64
+    with pytest.raises(b.NcError) as ei:
+        b.nc_op_matmul(1, 8, 8, 64, 0x1000, 8, 0, 0x2000, 64, 1, 0x3000, 8, None, 0, None)
+    assert ei.value.code == -7
     with pytest.raises(b.NcError) as ei:
         b.nc_op_matmul(1, 8, 8, 8, 0x1000, 8, 1, 0x2000, 8, 0, 0x3000, 8, None, 0, None)
     assert ei.value.code == -7

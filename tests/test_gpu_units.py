@@ -34,7 +34,10 @@ def _b():
     (512, 768, 4096, False),    # long k: split over the k loop
     (300, 520, 256, True),      # even k-tile count: persistent launch, ragged m and n tails
     (1, 8, 128, True),          # persistent launch, degenerate m, n
-    (512, 256, 2048, False),    # persistent launch, mn-major whole tiles, k split
+    (512, 256, 2048, False),    # mn-major whole tiles, k split
+    (300, 520, 192, "mixed"),   # k-major A, mn-major B (data-gradient layout), ragged tails
+    (512, 1280, 1280, "mixed"), # mixed layouts, whole tiles
+    (1, 8, 64, "mixed"),        # mixed layouts, degenerate m, n
 ])
 def test_matmul(dtype, M, N, K, kmajor):
     torch = require_gpu()
@@ -42,16 +45,22 @@ def test_matmul(dtype, M, N, K, kmajor):
     A = rand((M, K), 1, dtype=dtype)
     B = rand((N, K), 2, dtype=dtype)
     want = A.astype(np.float64) @ B.astype(np.float64).T
-    if kmajor:
-        Ad, Bd, lda, ldb = to_dev(A, dtype), to_dev(B, dtype), K, K
+    a_km = kmajor is True or kmajor == "mixed"
+    b_km = kmajor is True
+    mp, np_ = -(-M // 8) * 8, -(-N // 8) * 8
+    if a_km:
+        Ad, lda = to_dev(A, dtype), K
     else:
-        mp, np_ = -(-M // 8) * 8, -(-N // 8) * 8
         At = np.zeros((K, mp), np.float32); At[:, :M] = A.T
+        Ad, lda = to_dev(At, dtype), mp
+    if b_km:
+        Bd, ldb = to_dev(B, dtype), K
+    else:
         Bt = np.zeros((K, np_), np.float32); Bt[:, :N] = B.T
-        Ad, Bd, lda, ldb = to_dev(At, dtype), to_dev(Bt, dtype), mp, np_
+        Bd, ldb = to_dev(Bt, dtype), np_
     Cd = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
-    b.nc_op_matmul(DT[dtype], M, N, K, Ad.data_ptr(), lda, kmajor, Bd.data_ptr(), ldb, kmajor,
+    b.nc_op_matmul(DT[dtype], M, N, K, Ad.data_ptr(), lda, a_km, Bd.data_ptr(), ldb, b_km,
                    Cd.data_ptr(), N, ws.data_ptr(), ws.numel(), stream())
     torch.cuda.synchronize()
     got = from_dev(Cd)
