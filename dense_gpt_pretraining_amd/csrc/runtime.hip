@@ -157,8 +157,9 @@ Plan make_plan(const nc_config& c, bool bwd) {
         p.dk = take((size_t)N * hd * 4);
         p.dv = take((size_t)N * hd * 4);
         p.dqkv = take((size_t)N * Wq * es);
-        const int64_t wt_elems = std::max<int64_t>({D * Vp, D * F, D * Wq, H * hd * D});
-        p.wt = take((size_t)wt_elems * es);
+        // the unembedding weight transposed to [D][Vp] (the per-layer data
+        // gradients read their weights where they are stored)
+        p.wt = take((size_t)(D * Vp) * es);
         size_t sk = 0;
         sk = std::max(sk, nc::gemm_splitk_bytes((int)V, (int)D, (int)N));
         sk = std::max(sk, nc::gemm_splitk_bytes((int)D, (int)F, (int)N));
