@@ -387,14 +387,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
                 s = mfma32(lds_b128(sK + (rb0 + row_off[kk])), qf[kk], s);
                 dp = mfma32(lds_b128(sV + (rb0 + row_off[kk])), df[kk], dp);
             }
+            // keys past the row's position get the score -inf (p = 2^-inf = 0),
+            // in a loop of its own so that tiles off the diagonal branch past it
+            if (diag) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int key = kb + 32 * bi + 8 * (rr >> 2) + 4 * g + (rr & 3);
+                    if (key > t) s[rr] = -INFINITY;
+                }
+            }
             float ds[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                float p = ex2(fmaf(s[rr], scale_log2, nl2));
-                if (diag) {
-                    const int key = kb + 32 * bi + 8 * (rr >> 2) + 4 * g + (rr & 3);
-                    p = key > t ? 0.f : p;
-                }
+                const float p = ex2(fmaf(s[rr], scale_log2, nl2));
                 ds[rr] = p * (dp[rr] - dl);
             }
 #pragma unroll
@@ -653,8 +658,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
                 dp = mfma32(lds_b128(dr + row_off(kk)), lds_b128(vr + row_off(kk)), dp);
             }
             // lane holds key `key`; register rr holds row rb0 + 8(rr/4) + 4g + rr%4.
+            // Rows before the key's position get the score -inf (p = 2^-inf =
+            // 0), in a loop of its own so that blocks every row of which sees
+            // every key branch past it.
+            if (rb0 < w_all_vis) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    if (rb0 + 8 * (rr >> 2) + 4 * g + (rr & 3) < first_vis) s[rr] = -INFINITY;
+            }
             // P and dS are formed one 16-row half (registers 8h .. 8h+7) at a time.
-            const bool partial = rb0 < w_all_vis;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 float p[8], ds[8];
@@ -669,8 +681,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * m + e;
-                        float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
-                        if (partial) pv = (rb0 + 8 * m + 4 * g + e >= first_vis) ? pv : 0.f;
+                        const float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
                         p[4 * mm + e] = pv;
                         ds[4 * mm + e] = pv * (dp[rr] - dv4[e]);
                     }
