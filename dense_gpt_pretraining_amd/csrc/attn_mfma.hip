@@ -368,6 +368,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     f32x16_t acc[HD / 32];
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) acc[db] = zero16();
+    // dP - delta is formed by the product itself: its accumulator starts
+    // at -delta of the lane's row
+    f32x16_t ndl;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndl[i] = -dl;
 
     issue(0, sK0, sV0);
     // key tile it from (sK, sV); the next one is copied into (nK, nV)
@@ -380,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
         const bool diag = kb + kKT - 1 > tw_min;
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
-            f32x16_t s = zero16(), dp = zero16();
+            f32x16_t s = zero16(), dp = ndl;
             const int rb0 = bi * 32 * HD * 2;
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
@@ -400,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const float p = ex2(fmaf(s[rr], scale_log2, nl2));
-                ds[rr] = p * (dp[rr] - dl);
+                ds[rr] = p * dp[rr];
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
