@@ -33,7 +33,8 @@
 // the rescale is rare -- exact, because O and l always share the same stale
 // max.  Output O and the log-sum-exp per row.
 // Backward: dQ by a row-block kernel that recomputes P from the saved
-// log-sum-exp (and first forms delta = rowsum(dO * O) of its rows, which the
+// log-sum-exp (and first forms delta = rowsum(dO * O) of its rows; it hands
+// -delta and -lse log2 e of every row to the
 // next kernel reads); dK, dV by a key-block kernel that streams the query rows that
 // can see its keys, cut into chunks whose partial sums are added in chunk
 // order.  No atomics: the result is deterministic.
@@ -296,7 +297,8 @@ template <int HD, bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ o, const bf16_t* __restrict__ dout,
-    const float* __restrict__ lse, float* __restrict__ delta, float* __restrict__ dq, int B,
+    const float* __restrict__ lse, float* __restrict__ ndelta, float* __restrict__ nlse2,
+    float* __restrict__ dq, int B,
     int T, int H, float scale_log2, float scale, AttnBwdFuse fz) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
     // two buffers of a K and a V tile as four distinct arrays (see the
@@ -350,7 +352,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
         }
     }
     dl += __shfl_xor(dl, 32, 64);
-    if (valid && g == 0) delta[seq0 * H + r] = dl;
+    if (valid && g == 0) {
+        ndelta[seq0 * H + r] = -dl;
+        nlse2[seq0 * H + r] = nl2;
+    }
     const int last_row = min(r0 + kRB - 1, rows_total - 1);
     const int n_tiles = (last_row / H) / kKT + 1;
     const int w_first = r0 + 32 * w;
@@ -509,14 +514,14 @@ enum { kDkvPartials = 0, kDkvDirect = 1, kDkvFused = 2 };
 template <int HD, int OUT>
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-    int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dk_part, float* __restrict__ dv_part,
+    int64_t ldq, int64_t ldkv, const bf16_t* __restrict__ dout, const float* __restrict__ nlse2,
+    const float* __restrict__ ndelta, float* __restrict__ dk_part, float* __restrict__ dv_part,
     int B, int T, int H, float scale_log2, float scale, int chunk_rows, int slots_per_seq,
     AttnBwdFuse fz) {
     constexpr int TQ = kQT * HD * 2;              // bytes of a Q (or dO) row tile
     constexpr int RPI = 1024 / (HD * 2);          // tile rows per copy instruction
     constexpr int NI = TQ / 1024 / 8;             // copy instructions per wave per tile
-    constexpr int BUF = 2 * TQ + 2 * kQT * 4;     // Q | dO | lse | delta
+    constexpr int BUF = 2 * TQ + 2 * kQT * 4;     // Q | dO | -lse log2 e | -delta
     // two tile buffers, then the block's V rows (kKB x HD)
     __shared__ __align__(1024) char sm[2 * BUF + kKB * HD * 2];
     char* sV = sm + 2 * BUF;
@@ -589,8 +594,8 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     const int step_t = kQT / H, step_j = kQT - step_t * H;
     const char* qg = reinterpret_cast<const char*>(q + seq0 * ldq);
     const char* dg = reinterpret_cast<const char*>(dout + seq0 * H * HD);
-    const float* lg = lse + seq0 * H;
-    const float* eg = delta + seq0 * H;
+    const float* lg = nlse2 + seq0 * H;
+    const float* eg = ndelta + seq0 * H;
     // the Q rows of a tile span under kQT / H + 2 positions of the qkv buffer,
     // so offsets from the position of the tile's first row stay small
     auto issue = [&](int R0, int buf) {
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
             cp_t[i] += step_t;
             if (cp_j[i] >= H) { cp_j[i] -= H; cp_t[i] += 1; }
         }
-        // one wave copies the tile's log-sum-exp values, another its deltas
+        // one wave copies the tile's -lse log2 e values, another its -delta
         if (w == 0)
             lds_copy<4>(make_rsrc(lg + R0), lane * 4, sD + TQ);
         else if (w == 1)
@@ -679,16 +684,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
                 for (int mm = 0; mm < 2; ++mm) {
                     const int m = 2 * h + mm;
                     const int ro = 32 * qb + 8 * m + 4 * g;
+                    // p = 2^(s * scale_log2 - lse log2 e), dS = p (dP - delta)
                     const float4 l4 = *reinterpret_cast<const float4*>(sL + ro);
                     const float4 d4 = *reinterpret_cast<const float4*>(sL + kQT + ro);
                     const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                    const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const float nd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int rr = 4 * m + e;
-                        const float pv = ex2(fmaf(s[rr], scale_log2, -lv[e] * kLog2e));
+                        const float pv = ex2(fmaf(s[rr], scale_log2, lv[e]));
                         p[4 * mm + e] = pv;
-                        ds[4 * mm + e] = pv * (dp[rr] - dv4[e]);
+                        ds[4 * mm + e] = pv * (dp[rr] + nd[e]);
                     }
                 }
                 const bf16x8_t bp = pack8(p);
@@ -943,12 +949,15 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
                       float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
                       hipStream_t s, const AttnBwdFuse* fuse) {
     const AttnBwdFuse fz = fuse ? *fuse : AttnBwdFuse{};
-    // scratch: delta [B*T*H], then the dK and dV partials
-    float* delta = scratch;
+    // scratch: -delta [B*T*H], -lse log2 e [B*T*H], then the dK and dV
+    // partials
+    const int64_t nrow = ceil_div((int64_t)B * T * H, 64) * 64;
+    float* ndelta = scratch;
+    float* nlse2 = scratch + nrow;
     const int chunk = chunk_rows(B, T, H);
     const int slots = kv_slots_per_seq(T, H, chunk);
     const int64_t part = (int64_t)B * slots * kKB * HD;
-    float* dk_part = scratch + ceil_div((int64_t)B * T * H, 64) * 64;
+    float* dk_part = scratch + 2 * nrow;
     float* dv_part = dk_part + part;
     // algorithmic work of each kernel: causal (row, key) pairs times the
     // products the kernel forms per pair (2 HD flops each), and the bytes of
@@ -960,18 +969,20 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     const float scale = 1.f / sqrtf((float)HD);
     const float scale_log2 = kLog2e * scale;
     const int n_rb = (T * H + kRB - 1) / kRB;
-    // dq: delta = rowsum(dO * O), then S, dP and dQ
-    e = prof_label("attn_bwd_dq", 3 * 2.0 * HD * pairs, 3 * qo_b + 2 * kv_b + 8.0 * rows +
+    // dq: delta = rowsum(dO * O), then S, dP and dQ; reads lse, writes the
+    // two row values the dK/dV kernel reads
+    e = prof_label("attn_bwd_dq", 3 * 2.0 * HD * pairs, 3 * qo_b + 2 * kv_b + 12.0 * rows +
                                                             rows * HD * 4.0);
     if (e != hipSuccess) return e;
     // fused: dq~ goes through QK-norm and rotary backward into bf16 dqkv
     if (fuse)
         hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, true>), dim3(n_rb * B), dim3(256), 0, s, q, k,
-                           v, ldq, ldkv, o, dout, lse, delta, dq, B, T, H, scale_log2, scale, fz);
+                           v, ldq, ldkv, o, dout, lse, ndelta, nlse2, dq, B, T, H, scale_log2,
+                           scale, fz);
     else
         hipLaunchKernelGGL((k_attn_bwd_dq_mfma<HD, false>), dim3(n_rb * B), dim3(256), 0, s, q,
-                           k, v, ldq, ldkv, o, dout, lse, delta, dq, B, T, H, scale_log2, scale,
-                           fz);
+                           k, v, ldq, ldkv, o, dout, lse, ndelta, nlse2, dq, B, T, H, scale_log2,
+                           scale, fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dkv: S, dP, dV and dK; with one chunk per key block it finishes the
@@ -985,11 +996,11 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
         if (e != hipSuccess) return e;
         if (fuse)
             hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvFused>), dim3(slots * B), dim3(512), 0,
-                               s, q, k, v, ldq, ldkv, dout, lse, delta, dk, dv, B, T, H,
+                               s, q, k, v, ldq, ldkv, dout, nlse2, ndelta, dk, dv, B, T, H,
                                scale_log2, scale, chunk, slots, fz);
         else
             hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvDirect>), dim3(slots * B), dim3(512),
-                               0, s, q, k, v, ldq, ldkv, dout, lse, delta, dk, dv, B, T, H,
+                               0, s, q, k, v, ldq, ldkv, dout, nlse2, ndelta, dk, dv, B, T, H,
                                scale_log2, scale, chunk, slots, fz);
         return hipGetLastError();
     }
@@ -997,7 +1008,7 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
     e = prof_cut("attn_bwd_dkv", 4 * 2.0 * HD * pairs, 2 * qo_b + 2 * kv_b + 8.0 * rows + part_b);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_attn_bwd_dkv_mfma<HD, kDkvPartials>), dim3(slots * B), dim3(512), 0, s,
-                       q, k, v, ldq, ldkv, dout, lse, delta, dk_part, dv_part, B, T, H, scale_log2,
+                       q, k, v, ldq, ldkv, dout, nlse2, ndelta, dk_part, dv_part, B, T, H, scale_log2,
                        scale, chunk, slots, fz);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1041,9 +1052,9 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
 }
 
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd) {
-    const int64_t delta = ceil_div((int64_t)B * T * H, 64) * 64;
+    const int64_t nrow = ceil_div((int64_t)B * T * H, 64) * 64;
     const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, chunk_rows(B, T, H)) * kKB * hd;
-    return (size_t)(delta + 2 * part) * sizeof(float);
+    return (size_t)(2 * nrow + 2 * part) * sizeof(float);
 }
 
 }  // namespace nc

@@ -84,7 +84,8 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
                          int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
                          float* scratch, float* dq, float* dk, float* dv, int B, int T, int H,
                          int hd, hipStream_t s, const AttnBwdFuse* fuse = nullptr);
-// bytes of the scratch attn_bwd needs (row sums of dO*O and dK/dV partials)
+// bytes of the scratch attn_bwd needs (two values per query row: the row sum
+// of dO*O and the scaled log-sum-exp; then the dK/dV partials)
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 // Causal multi-query attention of B sequences of length T with H query heads
 // of width hd and one K/V head.  q: [B*T, H, hd] with token stride ldq;
