@@ -208,10 +208,12 @@ __device__ __forceinline__ void unpack_chunk<bf16_t>(const uint4& raw, float* ou
 }
 
 // tanh(y) = 1 - 2 / (exp(2y) + 1) on the hardware exp2 and reciprocal units;
-// saturates to +-1 (exp2 overflow gives 1/inf = 0).  Returns r = 1/(exp(2y)+1)
-// so that tanh = 1 - 2r and the softcapped logit is s (1 - 2r).
-__device__ __forceinline__ float tanh_r(float y) {
-    return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y * 2.8853900817779268f) + 1.f);
+// saturates to +-1 (exp2 overflow gives 1/inf = 0).  Takes y2 = 2 y log2 e
+// and returns r = 1/(exp(2y)+1), so that tanh = 1 - 2r and the softcapped
+// logit is s (1 - 2r).
+constexpr float kTwoLog2e = 2.8853900817779268f;
+__device__ __forceinline__ float tanh_r(float y2) {
+    return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y2) + 1.f);
 }
 
 // One wave per row.  The row's x and dn are read once into registers
@@ -274,7 +276,8 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     __shared__ float red[kCeThreads / 64];
     const int64_t row = blockIdx.x;
     T* zr = z + row * ldz;
-    const float inv_cap = 1.f / cap;
+    // the argument of tanh_r: z / s times 2 log2 e
+    const float zk = kTwoLog2e / cap;
     // exp(c) = 2^(s log2e (1 - 2r)) = 2^(a + b r)
     const float a = cap * kL2e, bb = -2.f * cap * kL2e;
     uint4 raw[MAXC];
@@ -289,11 +292,11 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
             if (c + VEC <= V) {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k)
-                    ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * inv_cap), a));
+                    ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * zk), a));
             } else {
 #pragma unroll
                 for (int k = 0; k < VEC; ++k)
-                    if (c + k < V) ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * inv_cap), a));
+                    if (c + k < V) ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * zk), a));
             }
         }
     }
@@ -301,14 +304,16 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     const float lse = __logf(ssum);
     const int y = tgt[row];
     if (threadIdx.x == 0) {
-        const float cy = cap * (1.f - 2.f * tanh_r(Elt<T>::ld(zr + y) * inv_cap));
+        const float cy = cap * (1.f - 2.f * tanh_r(Elt<T>::ld(zr + y) * zk));
         tok_loss[row] = lse - cy;
     }
     if (!want_grad) return;
     // every thread has finished reading z[y] before any thread overwrites it
     __syncthreads();
     const float sc = rowscale[row] * inv_n;
-    const float a2 = a - lse * kL2e;   // exp(c - lse) = 2^(a2 + b r)
+    // sc exp(c - lse) = 2^(a2 + b r): the row scale (positive) joins the
+    // exponent
+    const float a2 = a - lse * kL2e + __log2f(sc);
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int64_t c = ((int64_t)ci * kCeThreads + threadIdx.x) * VEC;
@@ -318,10 +323,10 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
 #pragma unroll
             for (int k = 0; k < VEC; ++k) {
                 // dL/dz = (softmax(c) - onehot) (1 - (c/s)^2) = (p - onehot) (1 - t^2)
-                const float r = tanh_r(v[k] * inv_cap);
+                const float r = tanh_r(v[k] * zk);
                 const float t = fmaf(-2.f, r, 1.f);
-                const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));
-                o[k] = sc * p * fmaf(-t, t, 1.f);
+                const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));   // sc softmax(c)
+                o[k] = p * fmaf(-t, t, 1.f);
             }
             if (c + VEC > V)
 #pragma unroll
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
 #pragma unroll
                 for (int k = 0; k < VEC; ++k)
                     if (c + k == y) {
-                        const float t = fmaf(-2.f, tanh_r(v[k] * inv_cap), 1.f);
+                        const float t = fmaf(-2.f, tanh_r(v[k] * zk), 1.f);
                         o[k] -= sc * fmaf(-t, t, 1.f);
                     }
             }
