@@ -303,8 +303,10 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     ssum = block_sum(ssum, red);
     const float lse = __logf(ssum);
     const int y = tgt[row];
+    float zy = 0.f;   // the target's raw logit (thread 0)
     if (threadIdx.x == 0) {
-        const float cy = cap * (1.f - 2.f * tanh_r(Elt<T>::ld(zr + y) * zk));
+        zy = Elt<T>::ld(zr + y);
+        const float cy = cap * (1.f - 2.f * tanh_r(zy * zk));
         tok_loss[row] = lse - cy;
     }
     if (!want_grad) return;
@@ -314,34 +316,38 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     // sc exp(c - lse) = 2^(a2 + b r): the row scale (positive) joins the
     // exponent
     const float a2 = a - lse * kL2e + __log2f(sc);
+    // dL/dz = (softmax(c) - onehot) (1 - (c/s)^2) = (p - onehot) (1 - t^2);
+    // this is its softmax part, sc p (1 - t^2)
+    auto grad = [&](float x) {
+        const float r = tanh_r(x * zk);
+        const float t = fmaf(-2.f, r, 1.f);
+        const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));   // sc softmax(c)
+        return p * fmaf(-t, t, 1.f);
+    };
+    // column indices fit in 32 bits: rows are at most 32 chunks per thread
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
-        const int64_t c = ((int64_t)ci * kCeThreads + threadIdx.x) * VEC;
+        const int c = (ci * kCeThreads + (int)threadIdx.x) * VEC;
         if (c < ldz) {
             float v[VEC], o[VEC];
             unpack_chunk<T>(raw[ci], v);
+            if (c + VEC <= V) {
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) {
-                // dL/dz = (softmax(c) - onehot) (1 - (c/s)^2) = (p - onehot) (1 - t^2)
-                const float r = tanh_r(v[k] * zk);
-                const float t = fmaf(-2.f, r, 1.f);
-                const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));   // sc softmax(c)
-                o[k] = p * fmaf(-t, t, 1.f);
-            }
-            if (c + VEC > V)
+                for (int k = 0; k < VEC; ++k) o[k] = grad(v[k]);
+            } else {
+                // the row's last valid chunk, and the padding columns (zero)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    if (c + k >= V) o[k] = 0.f;
-            if (y >= c && y < c + VEC) {
-#pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    if (c + k == y) {
-                        const float t = fmaf(-2.f, tanh_r(v[k] * zk), 1.f);
-                        o[k] -= sc * fmaf(-t, t, 1.f);
-                    }
+                for (int k = 0; k < VEC; ++k) o[k] = c + k < V ? grad(v[k]) : 0.f;
             }
             st_vec<T>(zr + c, o);
         }
+    }
+    // the target column also carries the onehot term: thread 0 rewrites it
+    // once every chunk store of the row has completed
+    __syncthreads();
+    if (threadIdx.x == 0 && y >= 0 && y < V) {   // ids out of range write nothing
+        const float t = fmaf(-2.f, tanh_r(zy * zk), 1.f);
+        Elt<T>::st(zr + y, grad(zy) - sc * fmaf(-t, t, 1.f));
     }
 }
 
