@@ -50,7 +50,8 @@ class nc_tensor_info(C.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m dense_gpt_pretraining_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python -m dense_gpt_pretraining_amd.build` "
+            "or `python -c 'import __graft_entry__; __graft_entry__.build()'`")
     return C.CDLL(LIB_PATH)
 
 
@@ -62,8 +63,10 @@ _sigs = {
                                   C.POINTER(C.c_int32)]),
     "nc_workspace_size": (C.c_int, [C.POINTER(nc_config), C.c_int32, C.POINTER(C.c_size_t)]),
     "nc_init_params": (C.c_int, [C.POINTER(nc_config), C.c_uint64, _P, _P]),
-    "nc_forward_loss": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
-    "nc_forward_backward": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P, _P,
+    "nc_forward_loss": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "nc_forward_token_loss": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
+                                        C.c_size_t, _P]),
+    "nc_forward_backward": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
                                       C.c_size_t, _P]),
     "nc_forward_backward_timed": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
                                             C.c_size_t, _P, C.POINTER(nc_kernel_stat),
@@ -138,15 +141,19 @@ def nc_init_params(cfg: nc_config, seed: int, params: int, stream: int):
     _check("nc_init_params", _lib.nc_init_params(C.byref(cfg), seed, params, stream))
 
 
-def nc_forward_loss(cfg, params, tokens, targets, loss, token_loss, ws, ws_bytes, stream):
+def nc_forward_loss(cfg, params, tokens, targets, loss, ws, ws_bytes, stream):
     _check("nc_forward_loss", _lib.nc_forward_loss(C.byref(cfg), params, tokens, targets, loss,
-                                                   token_loss, ws, ws_bytes, stream))
+                                                   ws, ws_bytes, stream))
 
 
-def nc_forward_backward(cfg, params, tokens, targets, loss, token_loss, grads, ws, ws_bytes,
-                        stream):
+def nc_forward_token_loss(cfg, params, tokens, targets, loss, token_loss, ws, ws_bytes, stream):
+    _check("nc_forward_token_loss", _lib.nc_forward_token_loss(
+        C.byref(cfg), params, tokens, targets, loss, token_loss, ws, ws_bytes, stream))
+
+
+def nc_forward_backward(cfg, params, tokens, targets, loss, grads, ws, ws_bytes, stream):
     _check("nc_forward_backward", _lib.nc_forward_backward(
-        C.byref(cfg), params, tokens, targets, loss, token_loss, grads, ws, ws_bytes, stream))
+        C.byref(cfg), params, tokens, targets, loss, grads, ws, ws_bytes, stream))
 
 
 def nc_forward_backward_timed(cfg, params, tokens, targets, loss, grads, ws, ws_bytes, stream,
@@ -211,6 +218,14 @@ def nc_op_rope_qknorm_fwd(dtype, B, T, H, hd, qkv, base, eps, rqk, tables, strea
                                                                eps, rqk, tables, stream))
 
 
+def _bf16_bits_rne(w: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even (the
+    library's own fp32 -> bf16 conversion; inputs are finite)."""
+    b = w.view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
 # ------------------------------------------------------------------ torch helper
 class Model:
     """Owns nothing but the config; allocates caller-side buffers with torch."""
@@ -237,7 +252,7 @@ class Model:
             flat = np.zeros(self.n_params, dtype=np.uint16)
             for name, off, r, c in self.layout:
                 w = np.ascontiguousarray(params[name], dtype=np.float32).reshape(-1)
-                flat[off:off + r * c] = (w.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+                flat[off:off + r * c] = _bf16_bits_rne(w)
             t = torch.from_numpy(flat.view(np.int16)).to(self.device)
             return t.view(torch.bfloat16)
         flat = np.zeros(self.n_params, dtype=np.float32)
@@ -280,20 +295,23 @@ class Model:
         loss = torch.empty(1, dtype=torch.float32, device=self.device)
         tl = torch.empty(tok.shape, dtype=torch.float32, device=self.device) if token_loss else None
         ws = self.workspace(False)
-        nc_forward_loss(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(),
-                        loss.data_ptr(), tl.data_ptr() if tl is not None else None,
-                        ws.data_ptr(), ws.numel(), self.stream())
-        return (loss, tl) if token_loss else loss
+        if tl is None:
+            nc_forward_loss(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(),
+                            loss.data_ptr(), ws.data_ptr(), ws.numel(), self.stream())
+            return loss
+        nc_forward_token_loss(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(),
+                              loss.data_ptr(), tl.data_ptr(), ws.data_ptr(), ws.numel(),
+                              self.stream())
+        return loss, tl
 
-    def forward_backward(self, params, tokens, targets, grads=None, token_loss: bool = False):
+    def forward_backward(self, params, tokens, targets, grads=None):
         torch = self.torch
         tok, tgt = self._tok(tokens), self._tok(targets)
         loss = torch.empty(1, dtype=torch.float32, device=self.device)
-        tl = torch.empty(tok.shape, dtype=torch.float32, device=self.device) if token_loss else None
         if grads is None:
             grads = torch.empty(self.n_params, dtype=torch.float32, device=self.device)
         ws = self.workspace(True)
         nc_forward_backward(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(),
-                            loss.data_ptr(), tl.data_ptr() if tl is not None else None,
-                            grads.data_ptr(), ws.data_ptr(), ws.numel(), self.stream())
-        return (loss, grads, tl) if token_loss else (loss, grads)
+                            loss.data_ptr(), grads.data_ptr(), ws.data_ptr(), ws.numel(),
+                            self.stream())
+        return loss, grads

@@ -1051,6 +1051,21 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
     return hipErrorInvalidValue;
 }
 
+template <>
+hipError_t attn_fwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
+                            int64_t ldkv, bf16_t* o, float* lse, int B, int Tn, int H, int hd,
+                            hipStream_t s) {
+    return attn_fwd_mfma(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
+}
+
+template <>
+hipError_t attn_bwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
+                            int64_t ldkv, const bf16_t* o, const bf16_t* dout, const float* lse,
+                            float* scratch, float* dq, float* dk, float* dv, int B, int Tn, int H,
+                            int hd, hipStream_t s) {
+    return attn_bwd_mfma(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, Tn, H, hd, s);
+}
+
 size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd) {
     const int64_t nrow = ceil_div((int64_t)B * T * H, 64) * 64;
     const int64_t part = (int64_t)B * kv_slots_per_seq(T, H, chunk_rows(B, T, H)) * kKB * hd;

@@ -1,5 +1,6 @@
-// Causal multi-query attention, plain per-row kernels (fp32 configuration,
-// and the reference path the matrix-core kernels are checked against).
+// Causal multi-query attention, plain per-row kernels: the attention of the
+// fp32 configuration (the bf16 configurations run the matrix-core kernels of
+// attn_mfma.hip).
 //
 // Multi-query attention (architecture list of the nanochat article): the H
 // query heads of a token share one key head and one value head.  Row (t, j)
@@ -209,15 +210,21 @@ hipError_t attn_bwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_
     return hipGetLastError();
 }
 
-#define NC_INST(T)                                                                              \
-    template hipError_t attn_fwd_simt<T>(const T*, const T*, const T*, int64_t, int64_t, T*,   \
-                                         float*, int, int, int, int, hipStream_t);             \
-    template hipError_t attn_delta<T>(const T*, const T*, int64_t, int, float*, hipStream_t);  \
-    template hipError_t attn_bwd_simt<T>(const T*, const T*, const T*, int64_t, int64_t,       \
-                                         const T*, const T*, const float*, float*, float*,     \
-                                         float*, float*, int, int, int, int, hipStream_t);
-NC_INST(float)
-NC_INST(bf16_t)
-#undef NC_INST
+template <>
+hipError_t attn_fwd<float>(const float* q, const float* k, const float* v, int64_t ldq,
+                           int64_t ldkv, float* o, float* lse, int B, int Tn, int H, int hd,
+                           hipStream_t s) {
+    return attn_fwd_simt<float>(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
+}
+
+template <>
+hipError_t attn_bwd<float>(const float* q, const float* k, const float* v, int64_t ldq,
+                           int64_t ldkv, const float* o, const float* dout, const float* lse,
+                           float* scratch, float* dq, float* dk, float* dv, int B, int Tn, int H,
+                           int hd, hipStream_t s) {
+    // the per-row kernels need only the row sums (first B*T*H floats)
+    return attn_bwd_simt<float>(q, k, v, ldq, ldkv, o, dout, lse, scratch, dq, dk, dv, B, Tn, H,
+                                hd, s);
+}
 
 }  // namespace nc

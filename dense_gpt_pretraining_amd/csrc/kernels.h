@@ -50,17 +50,8 @@ hipError_t gemm(int M, int N, int K, const T* A, int64_t lda, bool a_kmajor,
 size_t gemm_splitk_bytes(int M, int N, int K);
 
 // ----------------------------------------------------------------- attention
-// Per-row reference kernels (any T) and the dispatchers below.
-template <typename T>
-hipError_t attn_fwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_t ldkv, T* o,
-                         float* lse, int B, int Tn, int H, int hd, hipStream_t s);
-template <typename T>
-hipError_t attn_bwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_t ldkv,
-                         const T* o, const T* dout, const float* lse, float* delta, float* dq,
-                         float* dk, float* dv, int B, int Tn, int H, int hd, hipStream_t s);
-template <typename T>
-hipError_t attn_delta(const T* o, const T* dout, int64_t rows, int hd, float* delta,
-                      hipStream_t s);
+// attn_fwd / attn_bwd below run the per-row kernels of attn_simt.hip for
+// float and the matrix-core kernels for bf16.
 // Matrix-core kernels (bf16, T a multiple of 64, hd 64 or 128).
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,
@@ -139,6 +130,9 @@ template <typename T>
 hipError_t softcap_ce(T* z, int64_t ldz, int V, int N, const int32_t* tgt,
                       float cap, const float* rowscale, float inv_n,
                       float* tok_loss, bool want_grad, hipStream_t s);
+// widest logits row (ldz) softcap_ce takes for elements of elem_bytes bytes:
+// the kernel keeps a row in registers, 32 16-byte chunks per thread
+int64_t softcap_ce_max_ld(int elem_bytes);
 // loss = mean(tok_loss[0..N-1]) (fixed summation order)
 hipError_t mean_reduce(const float* x, int N, float* out, hipStream_t s);
 // out[c][r] = in[r][c] for a rows x cols matrix; out row stride ld_out;
@@ -146,7 +140,6 @@ hipError_t mean_reduce(const float* x, int N, float* out, hipStream_t s);
 template <typename T>
 hipError_t transpose(const T* in, int rows, int cols, int64_t ld_in, T* out,
                      int64_t ld_out, hipStream_t s);
-hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
 // ----------------------------------------------------------------- embedding grad
 // Deterministic scatter-add of de rows into dwte (fully overwritten):

@@ -114,7 +114,7 @@ int nc_op_softcap_ce(int32_t dtype, int32_t N, int32_t V, int64_t ldz, void* z,
     if (dtype != NC_F32 && dtype != NC_BF16) return NC_ERR_DTYPE;
     if (N < 1 || V < 2 || ldz < V || ldz % 8) return NC_ERR_CONFIG;
     if (!(softcap > 0.f) || softcap > 60.f) return NC_ERR_UNSUPPORTED;
-    if (ldz > (int64_t)32 * 256 * (dtype == NC_BF16 ? 8 : 4)) return NC_ERR_UNSUPPORTED;
+    if (ldz > nc::softcap_ce_max_ld(dtype == NC_BF16 ? 2 : 4)) return NC_ERR_UNSUPPORTED;
     if (!z || !targets || !tok_loss || (want_grad && !rowscale)) return NC_ERR_NULL;
     if (!al16(z) || !al16(targets) || !al16(tok_loss) || (rowscale && !al16(rowscale)))
         return NC_ERR_ALIGN;

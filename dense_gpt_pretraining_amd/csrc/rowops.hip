@@ -383,12 +383,6 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ in, int
     }
 }
 
-__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t k = i; k < n; k += stride) p[k] = v;
-}
-
 template <typename T>
 __global__ void k_zero(T* __restrict__ p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -559,12 +553,6 @@ hipError_t transpose(const T* in, int rows, int cols, int64_t ld_in, T* out, int
     return hipGetLastError();
 }
 
-hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
-    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, 256), 65536);
-    hipLaunchKernelGGL(k_fill_f32, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, s, p, n, v);
-    return hipGetLastError();
-}
-
 template <typename T>
 hipError_t zero_elems(T* p, int64_t n, hipStream_t s) {
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, 256), 65536);
@@ -580,6 +568,8 @@ hipError_t init_normal(T* p, int64_t n, float stdv, uint64_t seed, uint64_t stre
                        p, n, stdv, seed, stream_id);
     return hipGetLastError();
 }
+
+int64_t softcap_ce_max_ld(int elem_bytes) { return (int64_t)32 * kCeThreads * (16 / elem_bytes); }
 
 hipError_t count_bad_ids(const int32_t* a, const int32_t* b, int64_t n, int V, int32_t* n_bad,
                          hipStream_t s) {

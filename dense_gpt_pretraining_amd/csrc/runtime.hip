@@ -50,11 +50,11 @@ int validate(const nc_config* c) {
     if (c->seq_len % 64) return NC_ERR_UNSUPPORTED;
     if (c->softcap > 60.f) return NC_ERR_UNSUPPORTED;
     if (c->vocab > (1 << 24)) return NC_ERR_UNSUPPORTED;
-    // the fused cross-entropy keeps a padded vocabulary row in registers (32
-    // 16-byte chunks per thread of 512), and the norm backward a residual row
-    // (16 chunks per lane of 64)
+    // the fused cross-entropy keeps a padded vocabulary row in registers, and
+    // the norm backward a residual row (16 chunks per lane of 64)
     const int64_t vec = c->dtype == NC_BF16 ? 8 : 4;
-    if (vocab_pad(*c) > 32 * 512 * vec) return NC_ERR_UNSUPPORTED;
+    if (vocab_pad(*c) > nc::softcap_ce_max_ld(c->dtype == NC_BF16 ? 2 : 4))
+        return NC_ERR_UNSUPPORTED;
     if (c->d_model > 16 * 64 * vec) return NC_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)c->batch * c->seq_len;
     if (N > (1 << 24)) return NC_ERR_UNSUPPORTED;
@@ -600,8 +600,15 @@ int nc_init_params(const nc_config* cfg, uint64_t seed, void* params, void* stre
 }
 
 int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tokens,
-                    const int32_t* targets, float* loss, float* token_loss, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    const int32_t* targets, float* loss, void* ws, size_t ws_bytes,
+                    void* stream) {
+    return nc_forward_token_loss(cfg, params, tokens, targets, loss, nullptr, ws, ws_bytes,
+                                 stream);
+}
+
+int nc_forward_token_loss(const nc_config* cfg, const void* params, const int32_t* tokens,
+                          const int32_t* targets, float* loss, float* token_loss, void* ws,
+                          size_t ws_bytes, void* stream) {
     int rc = check_common(cfg, params, tokens, targets, loss, token_loss, ws);
     if (rc != NC_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -613,18 +620,17 @@ int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tok
 }
 
 int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t* tokens,
-                        const int32_t* targets, float* loss, float* token_loss, float* grads,
-                        void* ws, size_t ws_bytes, void* stream) {
-    int rc = check_common(cfg, params, tokens, targets, loss, token_loss, ws);
+                        const int32_t* targets, float* loss, float* grads, void* ws,
+                        size_t ws_bytes, void* stream) {
+    int rc = check_common(cfg, params, tokens, targets, loss, nullptr, ws);
     if (rc != NC_OK) return rc;
     if (!grads) return NC_ERR_NULL;
     if (!aligned(grads, 256)) return NC_ERR_ALIGN;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (cfg->dtype == NC_BF16)
-        return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, token_loss, grads, ws,
+        return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, nullptr, grads, ws,
                                     ws_bytes, s);
-    return run_step<float>(*cfg, params, tokens, targets, loss, token_loss, grads, ws, ws_bytes,
-                           s);
+    return run_step<float>(*cfg, params, tokens, targets, loss, nullptr, grads, ws, ws_bytes, s);
 }
 
 int nc_forward_backward_timed(const nc_config* cfg, const void* params, const int32_t* tokens,

@@ -133,13 +133,22 @@ int nc_init_params(const nc_config* cfg, uint64_t seed, void* params,
 /*
  * Forward pass and mean loss.  params: dtype per cfg, laid out as above.
  * tokens, targets: int32 [B, T].  loss: one fp32, the mean cross-entropy
- * over all B*T tokens (natural log).  token_loss: optional fp32 [B, T] of
- * per-token losses (NULL to skip).  ws: workspace of ws_bytes >=
+ * over all B*T tokens (natural log).  ws: workspace of ws_bytes >=
  * nc_workspace_size(cfg, 0).
  */
 int nc_forward_loss(const nc_config* cfg, const void* params,
                     const int32_t* tokens, const int32_t* targets, float* loss,
-                    float* token_loss, void* ws, size_t ws_bytes, void* stream);
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nc_forward_loss that also writes the per-token losses: token_loss fp32
+ * [B, T], l_t = logsumexp(c_t) - c_t[y_t] (NULL to skip, which is
+ * nc_forward_loss).  The mean loss is the mean of these values.
+ */
+int nc_forward_token_loss(const nc_config* cfg, const void* params,
+                          const int32_t* tokens, const int32_t* targets,
+                          float* loss, float* token_loss, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Forward and backward pass.  As nc_forward_loss, and `grads` (fp32, same
@@ -149,8 +158,8 @@ int nc_forward_loss(const nc_config* cfg, const void* params,
  */
 int nc_forward_backward(const nc_config* cfg, const void* params,
                         const int32_t* tokens, const int32_t* targets,
-                        float* loss, float* token_loss, float* grads, void* ws,
-                        size_t ws_bytes, void* stream);
+                        float* loss, float* grads, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* per-kernel account of one step (nc_forward_backward_timed) */
 typedef struct nc_kernel_stat {

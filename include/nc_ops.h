@@ -60,7 +60,8 @@ int nc_op_attention_bwd_scratch_bytes(int32_t B, int32_t T, int32_t H, int32_t h
 
 /*
  * Softcap + cross-entropy over the rows of z (T [N, ldz], V valid columns,
- * ldz a multiple of 8 and >= V): c = s tanh(z/s), tok_loss[t] =
+ * ldz a multiple of 8 and >= V, at most 131072 for bf16 and 65536 for fp32,
+ * else NC_ERR_UNSUPPORTED): c = s tanh(z/s), tok_loss[t] =
  * logsumexp(c_t) - c_t[y_t].  If want_grad, z is overwritten with
  * rowscale[t] * inv_n * (softmax(c_t) - onehot(y_t)) * (1 - (c_t/s)^2) and the
  * columns V..ldz-1 with zeros.  0 < s <= 60.

@@ -38,15 +38,37 @@ bf16 configurations) and are upcast on use.
 
 Query rows of attention and token rows of the cross-entropy are processed in
 chunks only to bound memory; every row is computed exactly as its definition
-states and rows never interact.
+states and rows never interact.  The query chunks of one sequence's attention
+run on a small thread pool; the key-side sums of the backward are then added
+in chunk order, so the result does not depend on the pool.  The forward-only
+cross-entropy runs its token chunks on the same pool.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 F64 = np.float64
 ATTN_QUERY_CHUNK = 1024
 CE_TOKEN_CHUNK = 2048
+ATTN_THREADS = max(1, min(4, len(os.sched_getaffinity(0))))
+
+
+def _chunks(n: int, size: int, fn):
+    """fn(t0, t1) for every chunk [t0, t1) of `size` rows out of n, on the
+    thread pool; the results are returned in chunk order."""
+    bounds = [(t0, min(n, t0 + size)) for t0 in range(0, n, size)]
+    if len(bounds) == 1 or ATTN_THREADS == 1:
+        return [fn(a, b) for a, b in bounds]
+    with ThreadPoolExecutor(max_workers=ATTN_THREADS) as ex:
+        return list(ex.map(lambda ab: fn(*ab), bounds))
+
+
+def _query_chunks(T: int, fn):
+    """fn(t0, t1) for every query chunk [t0, t1) of a length-T sequence."""
+    return _chunks(T, ATTN_QUERY_CHUNK, fn)
 
 
 # ---------------------------------------------------------------- primitives
@@ -124,13 +146,17 @@ def causal_mqa_attention(qn: np.ndarray, kn: np.ndarray, v: np.ndarray):
     scale = 1.0 / np.sqrt(hd)
     qh = np.ascontiguousarray(qn.transpose(1, 0, 2))          # [H, T, hd]
     o = np.empty((H, T, hd), dtype=F64)
-    for t0 in range(0, T, ATTN_QUERY_CHUNK):
-        t1 = min(T, t0 + ATTN_QUERY_CHUNK)
-        s = (qh[:, t0:t1, :] @ kn.T) * scale                   # [H, tq, T]
-        future = np.arange(T)[None, :] > np.arange(t0, t1)[:, None]
+
+    def chunk(t0, t1):
+        # keys past the chunk's last query (tau >= t1) take no part in the
+        # causal sum of any of its rows, so only keys 0 .. t1-1 are formed
+        s = (qh[:, t0:t1, :] @ kn[:t1].T) * scale              # [H, tq, t1]
+        future = np.arange(t1)[None, :] > np.arange(t0, t1)[:, None]
         s[:, future] = -np.inf
         p = _softmax_rows(s)
-        o[:, t0:t1, :] = p @ v
+        o[:, t0:t1, :] = p @ v[:t1]
+
+    _query_chunks(T, chunk)
     return np.ascontiguousarray(o.transpose(1, 0, 2))
 
 
@@ -148,18 +174,24 @@ def causal_mqa_attention_backward(qn, kn, v, do):
     dq = np.empty((H, T, hd), dtype=F64)
     dk = np.zeros((T, hd), dtype=F64)
     dv = np.zeros((T, hd), dtype=F64)
-    for t0 in range(0, T, ATTN_QUERY_CHUNK):
-        t1 = min(T, t0 + ATTN_QUERY_CHUNK)
-        s = (qh[:, t0:t1, :] @ kn.T) * scale
-        future = np.arange(T)[None, :] > np.arange(t0, t1)[:, None]
+
+    def chunk(t0, t1):
+        # as in the forward, keys tau >= t1 get no weight from these rows
+        s = (qh[:, t0:t1, :] @ kn[:t1].T) * scale
+        future = np.arange(t1)[None, :] > np.arange(t0, t1)[:, None]
         s[:, future] = -np.inf
-        p = _softmax_rows(s)                                   # [H, tq, T]
+        p = _softmax_rows(s)                                   # [H, tq, t1]
         d_o = doh[:, t0:t1, :]                                 # [H, tq, hd]
-        dv += np.einsum("hqk,hqd->kd", p, d_o, optimize=True)
-        dp = d_o @ v.T                                         # [H, tq, T]
+        dv_c = np.einsum("hqk,hqd->kd", p, d_o, optimize=True)
+        dp = d_o @ v[:t1].T                                    # [H, tq, t1]
         ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
-        dq[:, t0:t1, :] = (ds @ kn) * scale
-        dk += np.einsum("hqk,hqd->kd", ds, qh[:, t0:t1, :], optimize=True) * scale
+        dq[:, t0:t1, :] = (ds @ kn[:t1]) * scale
+        dk_c = np.einsum("hqk,hqd->kd", ds, qh[:, t0:t1, :], optimize=True) * scale
+        return t1, dk_c, dv_c
+
+    for t1, dk_c, dv_c in _query_chunks(T, chunk):
+        dk[:t1] += dk_c
+        dv[:t1] += dv_c
     return np.ascontiguousarray(dq.transpose(1, 0, 2)), dk, dv
 
 
@@ -277,6 +309,13 @@ def _head_loss(cfg, params, h, targets, want_grad):
     loss = np.empty(n, dtype=F64)
     df = np.empty((n, D), dtype=F64) if want_grad else None
     dwlm = np.zeros_like(wlm) if want_grad else None
+    if not want_grad:
+        # token chunks are independent: the forward alone runs them on the pool
+        def chunk(t0, t1):
+            loss[t0:t1] = softcap_cross_entropy(ff[t0:t1] @ wlm.T, y[t0:t1], cfg["softcap"])[0]
+
+        _chunks(n, CE_TOKEN_CHUNK, chunk)
+        return loss.reshape(B, T), None, None
     for t0 in range(0, n, CE_TOKEN_CHUNK):
         t1 = min(n, t0 + CE_TOKEN_CHUNK)
         z = ff[t0:t1] @ wlm.T

@@ -50,3 +50,24 @@ def cosine(got, want):
 def stream():
     import torch
     return torch.cuda.current_stream().cuda_stream
+
+
+def loss_deviation_errors(got_tok_loss, want_tok_loss, vocab):
+    """Per-token losses compared through their deviation from ln V.
+
+    A forward pass with any finite features gives losses near ln V when the
+    logits are small, so rel-L2 of the losses themselves says little; the
+    deviation l_t - ln V is what the features and the unembedding decide.
+    Returns (rel-L2, cosine) of the deviations."""
+    ln_v = np.log(float(vocab))
+    g = np.asarray(got_tok_loss, dtype=np.float64).ravel() - ln_v
+    w = np.asarray(want_tok_loss, dtype=np.float64).ravel() - ln_v
+    return rel_l2(g, w), cosine(g, w)
+
+
+# bar on the deviation: the bf16 path carries the residual stream in bf16
+# through every layer, which leaves its final features about 1% (relative)
+# from the float64 oracle's; the deviations inherit that error, so they are
+# held to the bar of a gradient tensor
+DEV_REL_L2 = 3e-2
+DEV_COS = 0.999

@@ -84,23 +84,73 @@ def test_null_and_alignment_and_workspace_errors_before_device_work():
     b = _b()
     c = b.make_config(get_config("tiny"))
     with pytest.raises(b.NcError) as ei:
-        b.nc_forward_loss(c, None, 256, 256, 256, None, 256, 1 << 20, None)
+        b.nc_forward_loss(c, None, 256, 256, 256, 256, 1 << 20, None)
     assert ei.value.code == -1
     with pytest.raises(b.NcError) as ei:
-        b.nc_forward_loss(c, 0x1000 + 8, 256, 256, 256, None, 512, 1 << 30, None)
+        b.nc_forward_loss(c, 0x1000 + 8, 256, 256, 256, 512, 1 << 30, None)
     assert ei.value.code == -5
     need = b.nc_workspace_size(c, False)
     with pytest.raises(b.NcError) as ei:
-        b.nc_forward_loss(c, 0x1000, 0x2000, 0x3000, 0x4000, None, 0x5000, need - 1, None)
+        b.nc_forward_loss(c, 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, need - 1, None)
+    assert ei.value.code == -4
+    with pytest.raises(b.NcError) as ei:
+        b.nc_forward_token_loss(c, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000 + 4, 0x5000, need,
+                                None)
+    assert ei.value.code == -5
+    with pytest.raises(b.NcError) as ei:
+        b.nc_forward_token_loss(c, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 0x5000, need - 1,
+                                None)
     assert ei.value.code == -4
     need_b = b.nc_workspace_size(c, True)
     with pytest.raises(b.NcError) as ei:
-        b.nc_forward_backward(c, 0x1000, 0x2000, 0x3000, 0x4000, None, 0x6000, 0x5000,
-                              need_b - 1, None)
+        b.nc_forward_backward(c, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000, 0x5000, need_b - 1,
+                              None)
     assert ei.value.code == -4
     with pytest.raises(b.NcError) as ei:
-        b.nc_forward_backward(c, 0x1000, 0x2000, 0x3000, 0x4000, None, None, 0x5000, need_b, None)
+        b.nc_forward_backward(c, 0x1000, 0x2000, 0x3000, 0x4000, None, 0x5000, need_b, None)
     assert ei.value.code == -1
+    with pytest.raises(b.NcError) as ei:
+        b.nc_forward_backward(c, 0x1000, 0x2000, 0x3000, 0x4000, 0x6000 + 16, 0x5000, need_b,
+                              None)
+    assert ei.value.code == -5
+
+
+def test_step_calls_have_the_three_call_boundary_signatures():
+    """nc_init_params, nc_forward_loss and nc_forward_backward take exactly the
+    arguments of the three-call boundary: (cfg, seed, params, stream),
+    (cfg, params, tokens, targets, loss, ws, ws_bytes, stream) and
+    (cfg, params, tokens, targets, loss, grads, ws, ws_bytes, stream)."""
+    with open(os.path.join(ROOT, "include", "nc.h")) as f:
+        text = " ".join(f.read().split())
+
+    def args(fn):
+        m = re.search(r"int " + fn + r"\(([^)]*)\);", text)
+        assert m, fn
+        return [a.strip().split()[-1].lstrip("*") for a in m.group(1).split(",")]
+
+    assert args("nc_init_params") == ["cfg", "seed", "params", "stream"]
+    assert args("nc_forward_loss") == ["cfg", "params", "tokens", "targets", "loss", "ws",
+                                       "ws_bytes", "stream"]
+    assert args("nc_forward_backward") == ["cfg", "params", "tokens", "targets", "loss",
+                                           "grads", "ws", "ws_bytes", "stream"]
+
+
+def test_pack_rounds_to_nearest_even():
+    """Model.pack converts fp32 to bf16 the way the library does (round to
+    nearest, ties to even), checked on values whose rounding is known."""
+    b = _b()
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9,
+                  -(1.0 + 2.0 ** -8 + 2.0 ** -12), 3.0e-3], dtype=np.float32)
+    bits = b._bf16_bits_rne(x.copy())
+    back = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0);
+    # 1 + 3*2^-8 ties between 1 + 2^-7 and 1 + 2^-6: even wins (1 + 2^-6)
+    assert back[0] == 1.0
+    assert back[1] == 1.0
+    assert back[2] == 1.0 + 2.0 ** -6
+    assert back[3] == 1.0
+    assert back[4] == -(1.0 + 2.0 ** -7)
+    assert abs(back[5] - np.float32(3.0e-3)) <= 2.0 ** -8 * 3.0e-3
 
 
 def test_layout_capacity_error():
@@ -133,3 +183,17 @@ def test_ops_validation():
     with pytest.raises(b.NcError) as ei:
         b.nc_op_softcap_ce(1, 4, 100, 96, 0x1000, 0x2000, 15.0, 0x3000, 0.25, 0x4000, 1, None)
     assert ei.value.code == -2
+    # the widest row the cross-entropy kernel holds: 131072 bf16 / 65536 fp32
+    # columns (the step's own vocabulary cap); one chunk more is refused
+    for dtype, cap in ((1, 131072), (0, 65536)):
+        with pytest.raises(b.NcError) as ei:
+            b.nc_op_softcap_ce(dtype, 4, 100, cap + 8, 0x1000, 0x2000, 15.0, 0x3000, 0.25,
+                               0x4000, 1, None)
+        assert ei.value.code == -7
+    for dtype, vocab in (("bf16", 131072), ("f32", 65536)):
+        c = b.make_config({**get_config("tiny"), "dtype": dtype, "vocab": vocab})
+        assert b.nc_param_count(c) > 0
+        c = b.make_config({**get_config("tiny"), "dtype": dtype, "vocab": vocab + 1})
+        with pytest.raises(b.NcError) as ei:
+            b.nc_param_count(c)
+        assert ei.value.code == -7

@@ -1,0 +1,89 @@
+"""GPU checks of the boundary calls that the parity tests do not exercise on
+their own: the contract of nc_init_params and the id count of
+nc_validate_tokens."""
+import numpy as np
+import pytest
+
+from nc_synth import get_config, make_tokens
+from tests.gpu_helpers import from_dev, require_gpu, stream
+
+pytestmark = pytest.mark.gpu
+
+
+def _b():
+    from dense_gpt_pretraining_amd import binding
+    return binding
+
+
+def _draw(m, seed):
+    torch = require_gpu()
+    p = torch.full((m.n_params,), 9.0, dtype=m.tdtype, device="cuda")
+    _b().nc_init_params(m.c, seed, p.data_ptr(), stream())
+    torch.cuda.synchronize()
+    return p
+
+
+@pytest.mark.parametrize("name", ["tiny", "d20"])
+def test_init_params_contract(name):
+    """Every matrix N(0, 0.02^2) and wlm N(0, 0.001^2): per-tensor sample mean
+    and standard deviation within 5 standard errors of their values, the
+    fraction within one sigma that of a normal law, padding exactly zero, the
+    same seed bitwise equal, another seed different, and distinct streams for
+    distinct tensors."""
+    from dense_gpt_pretraining_amd import Model
+    cfg = get_config(name)
+    m = Model(cfg)
+    p1 = _draw(m, 1234)
+    host = from_dev(p1)
+    covered = np.zeros(m.n_params, dtype=bool)
+    firsts = []
+    for n, off, r, c in m.layout:
+        w = host[off:off + r * c]
+        covered[off:off + r * c] = True
+        cnt = w.size
+        std = 0.001 if n == "wlm" else 0.02
+        mean, sd = w.mean(), w.std()
+        assert abs(mean) <= 5 * std / np.sqrt(cnt), (n, mean)
+        assert abs(sd - std) <= 5 * std / np.sqrt(2 * cnt) + 2 ** -9 * std, (n, sd)
+        inside = np.mean(np.abs(w) <= std)
+        assert abs(inside - 0.682689) <= 5 * np.sqrt(0.682689 * 0.317311 / cnt), (n, inside)
+        firsts.append(tuple(w[:8]))
+    # the padding between tensors is set to zero
+    assert np.all(host[~covered] == 0.0)
+    # distinct tensors draw from distinct streams
+    assert len(set(firsts)) == len(firsts)
+    p2 = _draw(m, 1234)
+    assert bool((p1.view(-1) == p2.view(-1)).all().item())
+    p3 = _draw(m, 1235)
+    same = float((p1 == p3).float().mean().item())
+    assert same < 0.05, same
+
+
+def test_validate_tokens_counts_planted_ids():
+    torch = require_gpu()
+    from dense_gpt_pretraining_amd import Model
+    cfg = get_config("gpt2", batch=4, seq_len=1024)
+    m = Model(cfg)
+    tokens, targets = make_tokens(cfg)
+    b = _b()
+    n_bad = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    tok = torch.from_numpy(tokens).cuda()
+    tgt = torch.from_numpy(targets).cuda()
+    b.nc_validate_tokens(m.c, tok.data_ptr(), tgt.data_ptr(), n_bad.data_ptr(), stream())
+    torch.cuda.synchronize()
+    assert int(n_bad.item()) == 0
+    rng = np.random.default_rng(4)
+    V = cfg["vocab"]
+    t2, y2 = tokens.copy(), targets.copy()
+    pos_t = rng.choice(t2.size, 37, replace=False)
+    pos_y = rng.choice(y2.size, 11, replace=False)
+    t2.reshape(-1)[pos_t] = rng.choice([-1, V, V + 7, -(1 << 30), (1 << 31) - 1], 37)
+    y2.reshape(-1)[pos_y] = rng.choice([-3, V, 2 * V], 11)
+    y2.reshape(-1)[0] = V - 1            # the largest valid id is not counted
+    tok = torch.from_numpy(t2).cuda()
+    tgt = torch.from_numpy(y2).cuda()
+    b.nc_validate_tokens(m.c, tok.data_ptr(), tgt.data_ptr(), n_bad.data_ptr(), stream())
+    torch.cuda.synchronize()
+    want = int(np.sum((t2 < 0) | (t2 >= V)) + np.sum((y2 < 0) | (y2 >= V)))
+    assert want == 37 + 11 - (1 if 0 in pos_y else 0)
+    assert int(n_bad.item()) == want

@@ -3,7 +3,9 @@ the float64 oracle on identical seeded inputs.
 
 Bar: the fp32 configuration matches in loss and every gradient tensor within
 1e-4 relative L2; bf16 configurations match the loss within 1e-2 relative and
-every gradient tensor within 3e-2 relative L2 with cosine >= 0.999.
+every gradient tensor within 3e-2 relative L2 with cosine >= 0.999.  The
+per-token losses are held to the gradient bar through their deviation from
+ln V.
 """
 import math
 
@@ -12,7 +14,7 @@ import pytest
 
 import oracle
 from nc_synth import get_config, make_params, make_tokens
-from tests.gpu_helpers import cosine, from_dev, rel_l2, require_gpu
+from tests.gpu_helpers import cosine, from_dev, loss_deviation_errors, rel_l2, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +28,7 @@ def _compare(cfg, params, tokens, targets, loss_tol, grad_tol, cos_min, label):
     torch = require_gpu()
     m = _model(cfg)
     p = m.pack(params)
-    loss, grads, tl = m.forward_backward(p, tokens, targets, token_loss=True)
+    loss, grads = m.forward_backward(p, tokens, targets)
     torch.cuda.synchronize()
     g = m.unpack(grads)
     want_loss, want = oracle.forward_backward(cfg, params, tokens, targets)
@@ -42,10 +44,18 @@ def _compare(cfg, params, tokens, targets, loss_tol, grad_tol, cos_min, label):
         assert c >= cos_min, (k, c)
     worst.sort(reverse=True)
     print(f"[{label}] worst grads: " + ", ".join(f"{k}:{e:.2e}/cos {c:.6f}" for e, k, c in worst[:4]))
-    # forward-only entry point agrees with the fused one
+    # forward-only entry points agree with the fused one
     l2 = m.forward_loss(p, tokens, targets)
+    l3, tl = m.forward_loss(p, tokens, targets, token_loss=True)
     torch.cuda.synchronize()
     assert abs(float(l2.item()) - got_loss) <= 1e-6 * abs(got_loss)
+    assert float(l3.item()) == float(l2.item())
+    # per-token losses through their deviation from ln V (the mean loss alone
+    # sits near ln V for any finite forward pass at small logits)
+    _, want_tl = oracle.forward_loss(cfg, params, tokens, targets)
+    e, c = loss_deviation_errors(from_dev(tl), want_tl, cfg["vocab"])
+    print(f"[{label}] per-token loss deviation from ln V: rel-L2 {e:.2e} cos {c:.6f}")
+    assert e < grad_tol and c >= cos_min, (e, c)
     return m, p, g
 
 

@@ -40,6 +40,21 @@ def _b():
     (1, 8, 64, "mixed"),        # mixed layouts, degenerate m, n
 ])
 def test_matmul(dtype, M, N, K, kmajor):
+    _matmul_case(dtype, M, N, K, kmajor)
+
+
+@pytest.mark.parametrize("M,N,K,kmajor", [
+    (300, 520, 200, True),      # k neither a multiple of 64 nor of the SIMT k tile
+    (264, 136, 1000, False),    # mn-major, ragged k
+    (65, 9, 7, True),           # k below one tile
+    (300, 520, 45, "mixed"),    # mixed layouts, ragged k
+])
+def test_matmul_fp32_ragged_k(M, N, K, kmajor):
+    """The fp32 product takes any K (the bf16 one requires a multiple of 64)."""
+    _matmul_case("f32", M, N, K, kmajor)
+
+
+def _matmul_case(dtype, M, N, K, kmajor):
     torch = require_gpu()
     b = _b()
     A = rand((M, K), 1, dtype=dtype)

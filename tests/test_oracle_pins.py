@@ -176,8 +176,14 @@ def test_attention_query_chunking_is_exact(monkeypatch):
     rng = _rng(10)
     q, k, v = rng.standard_normal((T, H, hd)), rng.standard_normal((T, hd)), rng.standard_normal((T, hd))
     full = oracle.causal_mqa_attention(q, k, v)
+    do = rng.standard_normal((T, H, hd))
+    full_b = oracle.causal_mqa_attention_backward(q, k, v, do)
     monkeypatch.setattr(om, "ATTN_QUERY_CHUNK", 16)
     np.testing.assert_allclose(oracle.causal_mqa_attention(q, k, v), full, rtol=1e-14, atol=1e-15)
+    # the backward's key-side sums over chunks (run on the thread pool, added
+    # in chunk order) equal the single-chunk result
+    for a, b in zip(oracle.causal_mqa_attention_backward(q, k, v, do), full_b):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
 
 
 # ----------------------------------------------------------------- softcap / CE
