@@ -108,6 +108,57 @@ def measured_traffic(config_name, label):
     return float(rec["bytes_per_launch"])
 
 
+OPTIM = dict(adam_lr=3e-3, adam_beta1=0.8, adam_beta2=0.95, adam_eps=1e-10,
+             adam_weight_decay=0.0, muon_lr=0.02, muon_momentum=0.95, muon_weight_decay=0.0,
+             muon_nesterov=1, muon_ns_steps=5, grad_clip=1.0)
+
+
+def optimizer_work(cfg, ns_steps):
+    """Algorithmic work of one optimizer step: Newton-Schulz flops (three
+    products per iteration per block matrix) and the HBM bytes of the
+    elementwise passes (AdamW: g, master, m, v read, master, m, v, param
+    written; Muon: momentum, X0 and update passes; the global norm reads g)."""
+    D, H, hd, F, V, L = (cfg[k] for k in ("d_model", "n_head", "head_dim", "d_mlp", "vocab",
+                                          "n_layer"))
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    flops, muon_elems = 0.0, 0
+    for r, c in ((H * hd, D), (hd, D), (hd, D), (D, H * hd), (F, D), (D, F)):
+        m, n = min(r, c), max(r, c)
+        flops += L * ns_steps * (2.0 * m * m * n + 2.0 * m * m * m + 2.0 * m * m * n)
+        muon_elems += L * r * c
+    adam_elems = 2 * V * D
+    nbytes = (adam_elems + muon_elems) * 4                       # global norm
+    nbytes += adam_elems * (4 + 3 * 8 + es)                      # AdamW
+    nbytes += muon_elems * ((4 + 8) + (4 + 4 + es) + (es + 8 + es))  # momentum, X0, update
+    return flops, nbytes
+
+
+def optimizer_timing(model, params, grads, cfg, steps):
+    """Mean duration of nc_optim_step (Muon + AdamW) on the workload's
+    parameters and the gradients of the last timed step."""
+    import torch
+
+    from dense_gpt_pretraining_amd import Optimizer
+    opt = Optimizer(model, OPTIM)
+    opt.init(params)
+    for t in range(1, 3):
+        opt.step(params, grads, t, 1.0)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for t in range(3, 3 + steps):
+        opt.step(params, grads, t, 1.0)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    flops, nbytes = optimizer_work(cfg, OPTIM["muon_ns_steps"])
+    return {"ms_per_step": round(ms, 3), "newton_schulz_tflop": round(flops / 1e12, 3),
+            "elementwise_gb": round(nbytes / 1e9, 3),
+            "note": "Muon (5 Newton-Schulz iterations, bf16 matrix cores) on every block matrix, "
+                    "AdamW on wte and wlm, global-norm clipping; not part of the fwd+bwd metric"}
+
+
 def cpu_baseline(cfg):
     """The oracle's fwd+bwd on one sequence of the workload, on host cores."""
     import numpy as np
@@ -138,6 +189,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d20")
     ap.add_argument("--profile-reps", type=int, default=3)
+    ap.add_argument("--optimizer", type=int, default=1,
+                    help="also time one Muon + AdamW optimizer step (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
@@ -208,6 +261,8 @@ def main():
         e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
         kernels.append(e)
 
+    optim = optimizer_timing(model, params, grads, cfg, 5) if args.optimizer else None
+
     cpu = cpu_baseline(cfg)
 
     out = {
@@ -233,6 +288,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "optimizer_step": optim,
         "kernels": kernels,
     }
     print(json.dumps(out))

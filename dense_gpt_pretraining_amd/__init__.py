@@ -13,7 +13,8 @@ _EXPORTS = (
     "Model", "NcError", "make_config", "nc_config", "nc_forward_backward", "nc_forward_loss",
     "nc_forward_token_loss", "nc_init_params", "nc_last_hip_error", "nc_param_count",
     "nc_param_layout", "nc_status_string", "nc_validate_tokens", "nc_workspace_size",
-    "NC_BF16", "NC_F32",
+    "NC_BF16", "NC_F32", "Optimizer", "make_optim_config", "nc_optim_step", "nc_optim_init",
+    "nc_grad_accumulate", "nc_lr_multiplier",
 )
 
 __all__ = list(_EXPORTS)

@@ -42,6 +42,13 @@ class nc_kernel_stat(C.Structure):
                 ("flops", C.c_double), ("bytes", C.c_double)]
 
 
+class nc_optim_config(C.Structure):
+    _fields_ = [(n, C.c_float) for n in (
+        "adam_lr", "adam_beta1", "adam_beta2", "adam_eps", "adam_weight_decay", "muon_lr",
+        "muon_momentum", "muon_weight_decay")] + [
+        ("muon_nesterov", C.c_int32), ("muon_ns_steps", C.c_int32), ("grad_clip", C.c_float)]
+
+
 class nc_tensor_info(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("offset", C.c_int64), ("rows", C.c_int32),
                 ("cols", C.c_int32)]
@@ -74,6 +81,13 @@ _sigs = {
     "nc_validate_tokens": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P]),
     "nc_status_string": (C.c_char_p, [C.c_int]),
     "nc_last_hip_error": (C.c_int, []),
+    "nc_optim_state_size": (C.c_int, [C.POINTER(nc_config), C.POINTER(C.c_size_t)]),
+    "nc_optim_workspace_size": (C.c_int, [C.POINTER(nc_config), C.POINTER(C.c_size_t)]),
+    "nc_optim_init": (C.c_int, [C.POINTER(nc_config), _P, _P, _P]),
+    "nc_optim_step": (C.c_int, [C.POINTER(nc_config), C.POINTER(nc_optim_config), C.c_int64,
+                                C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "nc_grad_accumulate": (C.c_int, [_P, _P, C.c_int64, C.c_float, C.c_int32, _P]),
+    "nc_lr_multiplier": (C.c_double, [C.c_int64, C.c_int64, C.c_int64, C.c_double]),
     "nc_op_matmul": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
                                C.c_int32, _P, C.c_int64, C.c_int32, _P, C.c_int64, _P,
                                C.c_size_t, _P]),
@@ -171,6 +185,49 @@ def nc_forward_backward_timed(cfg, params, tokens, targets, loss, grads, ws, ws_
 def nc_validate_tokens(cfg, tokens, targets, n_bad, stream):
     _check("nc_validate_tokens", _lib.nc_validate_tokens(C.byref(cfg), tokens, targets, n_bad,
                                                          stream))
+
+
+def make_optim_config(ocfg: dict) -> nc_optim_config:
+    """nc_optim_config from a dict with the field names of nc_optim.h."""
+    o = nc_optim_config()
+    for name, typ in nc_optim_config._fields_:
+        setattr(o, name, int(ocfg[name]) if typ is C.c_int32 else float(ocfg[name]))
+    return o
+
+
+def nc_optim_state_size(cfg: nc_config) -> int:
+    b = C.c_size_t()
+    _check("nc_optim_state_size", _lib.nc_optim_state_size(C.byref(cfg), C.byref(b)))
+    return b.value
+
+
+def nc_optim_workspace_size(cfg: nc_config) -> int:
+    b = C.c_size_t()
+    _check("nc_optim_workspace_size", _lib.nc_optim_workspace_size(C.byref(cfg), C.byref(b)))
+    return b.value
+
+
+def nc_optim_init(cfg, params, state, stream):
+    _check("nc_optim_init", _lib.nc_optim_init(C.byref(cfg), params, state, stream))
+
+
+def nc_optim_step(cfg, ocfg, step, lr_mult, grads, params, state, grad_norm, ws, ws_bytes,
+                  stream):
+    _check("nc_optim_step", _lib.nc_optim_step(C.byref(cfg), C.byref(ocfg), step, lr_mult,
+                                               grads, params, state, grad_norm, ws, ws_bytes,
+                                               stream))
+
+
+def nc_grad_accumulate(acc, grads, n, scale, overwrite, stream):
+    _check("nc_grad_accumulate", _lib.nc_grad_accumulate(acc, grads, n, scale, int(overwrite),
+                                                         stream))
+
+
+def nc_lr_multiplier(step: int, total: int, warmup: int, final_frac: float) -> float:
+    v = _lib.nc_lr_multiplier(step, total, warmup, final_frac)
+    if v < 0:
+        raise NcError("nc_lr_multiplier", -2, "a schedule argument is out of range")
+    return v
 
 
 def nc_status_string(code: int) -> str:
@@ -315,3 +372,41 @@ class Model:
                             loss.data_ptr(), grads.data_ptr(), ws.data_ptr(), ws.numel(),
                             self.stream())
         return loss, grads
+
+
+class Optimizer:
+    """Muon + AdamW state for a Model's parameters (device buffers from torch)."""
+
+    def __init__(self, model: Model, ocfg: dict):
+        torch = model.torch
+        self.m = model
+        self.o = make_optim_config(ocfg)
+        self.state = torch.empty(nc_optim_state_size(model.c), dtype=torch.uint8,
+                                 device=model.device)
+        self.ws = torch.empty(max(nc_optim_workspace_size(model.c), 256), dtype=torch.uint8,
+                              device=model.device)
+        self.norm = torch.empty(1, dtype=torch.float32, device=model.device)
+
+    def init(self, params):
+        nc_optim_init(self.m.c, params.data_ptr(), self.state.data_ptr(), self.m.stream())
+
+    def step(self, params, grads, step: int, lr_mult: float = 1.0):
+        """One step (step >= 1); returns the device tensor holding the global
+        gradient norm before clipping."""
+        nc_optim_step(self.m.c, self.o, step, lr_mult, grads.data_ptr(), params.data_ptr(),
+                      self.state.data_ptr(), self.norm.data_ptr(), self.ws.data_ptr(),
+                      self.ws.numel(), self.m.stream())
+        return self.norm
+
+    def master(self):
+        """fp32 master weights, unpacked per tensor (host arrays)."""
+        n = self.m.n_params
+        return self.m.unpack(self.state.view(self.m.torch.float32)[:n])
+
+    def moments(self):
+        """(first array, second array) of the state, unpacked per tensor."""
+        torch = self.m.torch
+        n = self.m.n_params
+        arr = ((n * 4 + 255) // 256) * 256 // 4
+        f = self.state.view(torch.float32)
+        return self.m.unpack(f[arr:arr + n]), self.m.unpack(f[2 * arr:2 * arr + n])

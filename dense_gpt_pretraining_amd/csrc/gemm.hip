@@ -49,11 +49,13 @@ struct EpiDev {
     float* rqk;
     int seq_len, n_head, head_dim;
     float eps;
+    float alpha, beta;
 };
 
 EpiDev make_epi(const Epilogue& p) {
     return EpiDev{p.mode,   p.rowscale, p.aux,     p.accumulate ? 1 : 0, p.cos_t, p.sin_t,
-                  p.rqk,    p.seq_len,  p.n_head,  p.head_dim,           p.eps};
+                  p.rqk,    p.seq_len,  p.n_head,  p.head_dim,           p.eps,   p.alpha,
+                  p.beta};
 }
 
 template <typename T>
@@ -67,6 +69,8 @@ __device__ __forceinline__ float epi_value(const EpiDev& e, int64_t m, int64_t i
         case EPI_RESID: return Elt<T>::ld(static_cast<const T*>(e.aux) + idx) + acc;
         case EPI_RELU2_BWD:
             return e.rowscale[m] * acc * 2.f * sqrtf(Elt<T>::ld(static_cast<const T*>(e.aux) + idx));
+        case EPI_AXPBY:
+            return e.alpha * Elt<T>::ld(static_cast<const T*>(e.aux) + idx) + e.beta * acc;
         default: return acc;  // EPI_STORE_T
     }
 }
@@ -90,7 +94,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_gemm_simt(int M, int N, int K, const T* __restrict__ A,
                                                    int64_t lda, int ak, const T* __restrict__ B,
                                                    int64_t ldb, int bk, void* C, int64_t ldc,
-                                                   EpiDev e) {
+                                                   EpiDev e, int64_t bsa, int64_t bsb,
+                                                   int64_t bsc) {
+    // product blockIdx.z of a batch
+    const int64_t bz = blockIdx.z;
+    A += bz * bsa;
+    B += bz * bsb;
+    if (e.mode == EPI_STORE_F32) C = static_cast<float*>(C) + bz * bsc;
+    else C = static_cast<T*>(C) + bz * bsc;
+    if (e.aux) e.aux = static_cast<const T*>(e.aux) + bz * bsc;
     __shared__ float As[kSK][kSB + 4];
     __shared__ float Bs[kSK][kSB + 4];
     const int m0 = blockIdx.y * kSB, n0 = blockIdx.x * kSB;
@@ -283,12 +295,15 @@ __device__ __forceinline__ void epi_vec4(const EpiDev& e, void* C, int64_t idx, 
         st_nt(c, o);
     } else {
         float o[4] = {v0, v1, v2, v3};
-        if (MODE == EPI_RESID || MODE == EPI_RELU2_BWD) {
+        if (MODE == EPI_RESID || MODE == EPI_RELU2_BWD || MODE == EPI_AXPBY) {
             const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(e.aux) + idx);
             const float x[4] = {bf_lo(a.x), bf_hi(a.x), bf_lo(a.y), bf_hi(a.y)};
             if (MODE == EPI_RESID) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) o[q] += x[q];
+            } else if (MODE == EPI_AXPBY) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) o[q] = e.alpha * x[q] + e.beta * o[q];
             } else {
                 const float rs = 2.f * e.rowscale[m];
 #pragma unroll
@@ -323,6 +338,7 @@ __device__ __forceinline__ void epi_vec4_pre(const EpiDev& e, void* C, int64_t i
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (MODE == EPI_RESID) o[q] += x[q];
+        if (MODE == EPI_AXPBY) o[q] = e.alpha * x[q] + e.beta * o[q];
         if (MODE == EPI_RELU2_BWD) o[q] *= 2.f * rs * __builtin_amdgcn_sqrtf(x[q]);
         if (MODE == EPI_ROWSCALE) o[q] *= rs;
         if (MODE == EPI_ROWSCALE_RELU2) {
@@ -458,7 +474,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                                                            int64_t lda,
                                                            const bf16_t* __restrict__ B,
                                                            int64_t ldb, void* C, int64_t ldc,
-                                                           EpiDev e, int64_t split_stride) {
+                                                           EpiDev e, int64_t split_stride,
+                                                           int64_t bsa, int64_t bsb,
+                                                           int64_t bsc) {
     // two buffers of an A tile and a B tile, as four distinct arrays: with the
     // buffer known at compile time (the k loop is unrolled by two) and one
     // byte offset from the array's start per access, the compiler can see
@@ -489,6 +507,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     const int ke = min(K, kb + k_per_split);
     if (MODE == EPI_STORE_F32 && split_stride)
         C = static_cast<float*>(C) + split * split_stride;
+    // product blockIdx.y of a batch (the batched products run unsplit)
+    {
+        const int64_t bz = blockIdx.y;
+        A += bz * bsa;
+        B += bz * bsb;
+        if (MODE == EPI_STORE_F32) C = static_cast<float*>(C) + bz * bsc;
+        else C = static_cast<bf16_t*>(C) + bz * bsc;
+        if (MODE == EPI_RESID || MODE == EPI_RELU2_BWD || MODE == EPI_AXPBY)
+            e.aux = static_cast<const bf16_t*>(e.aux) + bz * bsc;
+    }
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -537,7 +565,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         else mn_issue(B + (int64_t)k0 * ldb + n0, mb, tb, wave);
     };
     // the epilogue's aux rows (x of the residual, g of the relu^2 backward)
-    constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD;
+    constexpr bool kAux = MODE == EPI_RESID || MODE == EPI_RELU2_BWD || MODE == EPI_AXPBY;
     const int li = lane & 31, hi = lane >> 5;
     const bool full_n = n0 + kTN <= N;
     auto load_aux = [&](int j, uint2 (&dst)[16]) {
@@ -757,14 +785,15 @@ int choose_splits(int M, int N, int K) {
 template <bool AK, bool BK, int MODE>
 hipError_t launch_mfma(int M, int N, int K, const bf16_t* A, int64_t lda, const bf16_t* B,
                        int64_t ldb, void* C, int64_t ldc, const EpiDev& e, int splits,
-                       int64_t split_stride, hipStream_t s) {
+                       int64_t split_stride, hipStream_t s, const GemmBatch& bt) {
     int k_per = (int)ceil_div(K, splits);
     k_per = (int)ceil_div(k_per, kTK) * kTK;
     const int tiles = (int)(ceil_div(M, kTM) * ceil_div(N, kTN));
     auto kern = k_gemm_mfma<AK, BK, MODE>;
-    // one workgroup per (split, tile) item
-    hipLaunchKernelGGL(kern, dim3(tiles * splits, 1, 1), dim3(kThreads), 0, s, M, N, K, k_per,
-                       splits, A, lda, B, ldb, C, ldc, e, split_stride);
+    // one workgroup per (split, tile) item and product of the batch
+    hipLaunchKernelGGL(kern, dim3(tiles * splits, bt.count, 1), dim3(kThreads), 0, s, M, N, K,
+                       k_per, splits, A, lda, B, ldb, C, ldc, e, split_stride, bt.sa, bt.sb,
+                       bt.sc);
     return hipGetLastError();
 }
 
@@ -781,13 +810,17 @@ size_t gemm_splitk_bytes(int M, int N, int K) {
 template <>
 hipError_t gemm<float>(int M, int N, int K, const float* A, int64_t lda, bool a_kmajor,
                        const float* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
-                       const Epilogue& epi, float*, size_t, hipStream_t s) {
-    if (M <= 0 || N <= 0) return hipSuccess;
+                       const Epilogue& epi, float*, size_t, hipStream_t s,
+                       const GemmBatch* batch) {
+    const GemmBatch bt = batch ? *batch : GemmBatch{};
+    if (M <= 0 || N <= 0 || bt.count <= 0) return hipSuccess;
     if (epi.mode == EPI_QKV_ROPE) return hipErrorInvalidValue;   // bf16 only
+    if (bt.count > 1 && epi.rowscale) return hipErrorInvalidValue;
     const EpiDev e = make_epi(epi);
-    dim3 grid((unsigned)ceil_div(N, kSB), (unsigned)ceil_div(M, kSB));
+    dim3 grid((unsigned)ceil_div(N, kSB), (unsigned)ceil_div(M, kSB), (unsigned)bt.count);
     hipLaunchKernelGGL(k_gemm_simt<float>, grid, dim3(256), 0, s, M, N, K, A, lda,
-                       a_kmajor ? 1 : 0, B, ldb, b_kmajor ? 1 : 0, C, ldc, e);
+                       a_kmajor ? 1 : 0, B, ldb, b_kmajor ? 1 : 0, C, ldc, e, bt.sa, bt.sb,
+                       bt.sc);
     return hipGetLastError();
 }
 
@@ -795,15 +828,17 @@ template <>
 hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool a_kmajor,
                         const bf16_t* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
                         const Epilogue& epi, float* splitk_ws, size_t splitk_ws_bytes,
-                        hipStream_t s) {
-    if (M <= 0 || N <= 0) return hipSuccess;
+                        hipStream_t s, const GemmBatch* batch) {
+    const GemmBatch bt = batch ? *batch : GemmBatch{};
+    if (M <= 0 || N <= 0 || bt.count <= 0) return hipSuccess;
+    if (bt.count > 1 && (epi.rowscale || epi.mode == EPI_QKV_ROPE)) return hipErrorInvalidValue;
     const EpiDev e = make_epi(epi);
     if (epi.mode == EPI_QKV_ROPE &&
         (epi.head_dim <= 0 || 128 % epi.head_dim || epi.head_dim % 8 || !epi.cos_t ||
          !epi.sin_t || !epi.rqk || epi.seq_len <= 0 || N != (epi.n_head + 2) * epi.head_dim))
         return hipErrorInvalidValue;
     int splits = 1;
-    if (epi.mode == EPI_STORE_F32) {
+    if (epi.mode == EPI_STORE_F32 && bt.count == 1) {
         splits = choose_splits(M, N, K);
         if (gemm_splitk_bytes(M, N, K) > splitk_ws_bytes || splitk_ws == nullptr) splits = 1;
     }
@@ -822,37 +857,45 @@ hipError_t gemm<bf16_t>(int M, int N, int K, const bf16_t* A, int64_t lda, bool 
     if (a_kmajor && b_kmajor) {
         switch (epi.mode) {
             case EPI_STORE_F32:
-                err = launch_mfma<true, true, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_ROWSCALE:
-                err = launch_mfma<true, true, EPI_ROWSCALE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_ROWSCALE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_ROWSCALE_RELU2:
-                err = launch_mfma<true, true, EPI_ROWSCALE_RELU2>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_ROWSCALE_RELU2>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_RESID:
-                err = launch_mfma<true, true, EPI_RESID>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_RESID>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_RELU2_BWD:
-                err = launch_mfma<true, true, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_STORE_T:
-                err = launch_mfma<true, true, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             case EPI_QKV_ROPE:
-                err = launch_mfma<true, true, EPI_QKV_ROPE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+                err = launch_mfma<true, true, EPI_QKV_ROPE>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
+                break;
+            case EPI_AXPBY:
+                err = launch_mfma<true, true, EPI_AXPBY>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
                 break;
             default: return hipErrorInvalidValue;
         }
     } else if (!a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
-        err = launch_mfma<false, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+        err = launch_mfma<false, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
+    } else if (!a_kmajor && !b_kmajor && epi.mode == EPI_STORE_T) {
+        // Gram matrix X^T X of a tall matrix (orthogonalisation)
+        err = launch_mfma<false, false, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
+    } else if (a_kmajor && !b_kmajor && epi.mode == EPI_AXPBY) {
+        err = launch_mfma<true, false, EPI_AXPBY>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
     } else if (a_kmajor && !b_kmajor && epi.mode == EPI_STORE_F32) {
-        err = launch_mfma<true, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+        err = launch_mfma<true, false, EPI_STORE_F32>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
     } else if (a_kmajor && !b_kmajor && epi.mode == EPI_STORE_T) {
         // data gradients dX = dY W straight from the [out][in] weight
-        err = launch_mfma<true, false, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+        err = launch_mfma<true, false, EPI_STORE_T>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
     } else if (a_kmajor && !b_kmajor && epi.mode == EPI_RELU2_BWD) {
-        err = launch_mfma<true, false, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s);
+        err = launch_mfma<true, false, EPI_RELU2_BWD>(M, N, K, A, lda, B, ldb, out, ld_out, ek, splits, stride, s, bt);
     } else {
         return hipErrorInvalidValue;  // layout/epilogue pair the step never uses
     }

@@ -27,6 +27,7 @@ enum EpiMode : int {
     // receives each head's 1/rms; the value head is stored as u.  bf16 only;
     // head_dim must divide 128.
     EPI_QKV_ROPE = 6,
+    EPI_AXPBY = 7,       // C[m][n] = alpha * aux[m][n] + beta * acc (aux: T, ld = ldc)
 };
 struct Epilogue {
     int mode = EPI_STORE_F32;
@@ -39,13 +40,22 @@ struct Epilogue {
     float* rqk = nullptr;           // [M, n_head + 1]
     int seq_len = 0, n_head = 0, head_dim = 0;
     float eps = 0.f;
+    // EPI_AXPBY
+    float alpha = 1.f, beta = 1.f;
+};
+// A batch of independent products of one shape: product i reads A + i*sa,
+// B + i*sb and writes C + i*sc (the epilogue's aux at the same offset as C);
+// elements of the operand and output types.  No k split, no row scale.
+struct GemmBatch {
+    int count = 1;
+    int64_t sa = 0, sb = 0, sc = 0;
 };
 
 template <typename T>
 hipError_t gemm(int M, int N, int K, const T* A, int64_t lda, bool a_kmajor,
                 const T* B, int64_t ldb, bool b_kmajor, void* C, int64_t ldc,
                 const Epilogue& epi, float* splitk_ws, size_t splitk_ws_bytes,
-                hipStream_t s);
+                hipStream_t s, const GemmBatch* batch = nullptr);
 // bytes of split-K scratch gemm() may use for an fp32 output of M x N
 size_t gemm_splitk_bytes(int M, int N, int K);
 

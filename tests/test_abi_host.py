@@ -20,7 +20,9 @@ def _b():
 
 def _declared():
     names = set()
-    for h in ("nc.h", "nc_ops.h"):
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
         with open(os.path.join(ROOT, "include", h)) as f:
             text = f.read()
         names |= set(re.findall(r"\b(nc_\w+)\s*\(", text))
@@ -197,3 +199,55 @@ def test_ops_validation():
         with pytest.raises(b.NcError) as ei:
             b.nc_param_count(c)
         assert ei.value.code == -7
+
+
+OCFG = dict(adam_lr=3e-3, adam_beta1=0.8, adam_beta2=0.95, adam_eps=1e-10,
+            adam_weight_decay=0.0, muon_lr=0.02, muon_momentum=0.95, muon_weight_decay=0.0,
+            muon_nesterov=1, muon_ns_steps=5, grad_clip=1.0)
+
+
+def test_lr_multiplier_matches_the_oracle_schedule():
+    """The library's host-side schedule against the oracle's, step by step."""
+    import oracle.optim as oo
+    b = _b()
+    for total, warmup, f in ((100, 10, 0.1), (50, 0, 0.0), (7, 7, 1.0), (1000, 37, 0.25)):
+        for step in list(range(0, total + 3)) + [10 * total]:
+            assert b.nc_lr_multiplier(step, total, warmup, f) == pytest.approx(
+                oo.lr_multiplier(step, total, warmup, f), rel=1e-14, abs=1e-15)
+    for args in ((0, 0, 0, 0.1), (0, 10, -1, 0.1), (0, 10, 1, 1.5), (-1, 10, 1, 0.1)):
+        with pytest.raises(b.NcError):
+            b.nc_lr_multiplier(*args)
+
+
+def test_optimizer_validation_before_device_work():
+    b = _b()
+    c = b.make_config(get_config("tiny"))
+    ws = b.nc_optim_workspace_size(c)
+    st = b.nc_optim_state_size(c)
+    n = b.nc_param_count(c)
+    assert st == 3 * (((n * 4 + 255) // 256) * 256)
+    assert ws > 0
+    o = b.make_optim_config(OCFG)
+    args = lambda **kw: dict(dict(step=1, lr_mult=1.0, grads=0x1000, params=0x2000, state=0x3000,
+                                  norm=None, ws=0x4000, wsb=ws), **kw)
+
+    def call(oc=o, **kw):
+        a = args(**kw)
+        b.nc_optim_step(c, oc, a["step"], a["lr_mult"], a["grads"], a["params"], a["state"],
+                        a["norm"], a["ws"], a["wsb"], None)
+
+    for kw, code in ((dict(step=0), -2), (dict(lr_mult=-1.0), -2), (dict(grads=None), -1),
+                     (dict(params=0x2000 + 16), -5), (dict(norm=0x5002), -5),
+                     (dict(wsb=ws - 1), -4)):
+        with pytest.raises(b.NcError) as ei:
+            call(**kw)
+        assert ei.value.code == code, kw
+    for field, value in (("adam_beta1", 1.0), ("adam_eps", 0.0), ("muon_momentum", -0.1),
+                         ("muon_ns_steps", 17), ("grad_clip", -1.0), ("muon_nesterov", 2),
+                         ("adam_lr", float("nan"))):
+        with pytest.raises(b.NcError) as ei:
+            call(oc=b.make_optim_config({**OCFG, field: value}))
+        assert ei.value.code == -2, field
+    with pytest.raises(b.NcError) as ei:
+        b.nc_grad_accumulate(0x1000 + 4, 0x2000, 10, 0.5, 0, None)
+    assert ei.value.code == -5

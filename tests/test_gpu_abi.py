@@ -1,6 +1,8 @@
 """GPU checks of the boundary calls that the parity tests do not exercise on
 their own: the contract of nc_init_params and the id count of
 nc_validate_tokens."""
+import math
+
 import numpy as np
 import pytest
 
@@ -13,6 +15,14 @@ pytestmark = pytest.mark.gpu
 def _b():
     from dense_gpt_pretraining_amd import binding
     return binding
+
+
+def _bf16_inside_limit(x):
+    """Midpoint between the largest bf16 value <= x and the next one up."""
+    b = np.float32(x).view(np.uint32) & np.uint32(0xFFFF0000)
+    lo = np.array([b], np.uint32).view(np.float32)[0]
+    hi = np.array([b + np.uint32(0x10000)], np.uint32).view(np.float32)[0]
+    return 0.5 * (float(lo) + float(hi))
 
 
 def _draw(m, seed):
@@ -45,8 +55,13 @@ def test_init_params_contract(name):
         mean, sd = w.mean(), w.std()
         assert abs(mean) <= 5 * std / np.sqrt(cnt), (n, mean)
         assert abs(sd - std) <= 5 * std / np.sqrt(2 * cnt) + 2 ** -9 * std, (n, sd)
+        # P(|x| <= std) of the stored values: a bf16 value is <= std exactly
+        # when the drawn value lies below the midpoint of the two bf16
+        # neighbours of std
+        lim = _bf16_inside_limit(std) if cfg["dtype"] == "bf16" else std
+        p_in = math.erf(lim / std / math.sqrt(2.0))
         inside = np.mean(np.abs(w) <= std)
-        assert abs(inside - 0.682689) <= 5 * np.sqrt(0.682689 * 0.317311 / cnt), (n, inside)
+        assert abs(inside - p_in) <= 5 * np.sqrt(p_in * (1 - p_in) / cnt), (n, inside, p_in)
         firsts.append(tuple(w[:8]))
     # the padding between tensors is set to zero
     assert np.all(host[~covered] == 0.0)

@@ -1,0 +1,195 @@
+"""GPU parity of the optimizer step (include/nc_optim.h) with the float64
+oracle (oracle/optim.py) on identical seeded parameters and gradients.
+
+Bars, from the arithmetic of each part:
+* AdamW and every elementwise pass run in fp32 on both configurations: the
+  weight change of each AdamW tensor, the moments, Muon's momentum buffer and
+  the gradient norm within 1e-5 relative L2;
+* Muon's Newton-Schulz iteration runs in fp32 for the fp32 configuration
+  (weight change within 1e-4 relative L2) and on bf16 matrix cores for the
+  bf16 ones, where each stored matrix is rounded to bf16: the weight change
+  of each Muon tensor within 3e-2 relative L2 with cosine >= 0.999 (the bf16
+  bar of the step's gradients);
+* the parameters written are the fp32 master weights rounded to the
+  parameter type (round to nearest even), bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.optim as oo
+from nc_synth import bf16_bits, get_config, make_params, make_tokens
+from tests.gpu_helpers import cosine, from_dev, rel_l2, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+OCFG = dict(adam_lr=3e-3, adam_beta1=0.8, adam_beta2=0.95, adam_eps=1e-10,
+            adam_weight_decay=0.01, muon_lr=0.02, muon_momentum=0.95, muon_weight_decay=0.01,
+            muon_nesterov=1, muon_ns_steps=5, grad_clip=1.0)
+
+
+def _flat_f32(m, tensors):
+    """fp32 device buffer in the parameter layout (padding zero)."""
+    torch = require_gpu()
+    flat = np.zeros(m.n_params, np.float32)
+    for name, off, r, c in m.layout:
+        flat[off:off + r * c] = np.asarray(tensors[name], np.float32).reshape(-1)
+    return torch.from_numpy(flat).cuda()
+
+
+def _grads(params, seed):
+    rng = np.random.default_rng(seed)
+    out = {}
+    for k, v in params.items():
+        scale = 1e-3 if k in ("wte", "wlm") else 1e-2
+        out[k] = (rng.standard_normal(v.shape) * scale).astype(np.float32)
+    return out
+
+
+def _run_steps(cfg, ocfg, n_steps, lr_mults):
+    from dense_gpt_pretraining_amd import Model, Optimizer
+    torch = require_gpu()
+    params = make_params(cfg)
+    m = Model(cfg)
+    p = m.pack(params)
+    opt = Optimizer(m, ocfg)
+    opt.init(p)
+    st = oo.init_state(params)
+    bf16 = cfg["dtype"] == "bf16"
+    ns_tol = 3e-2 if bf16 else 1e-4
+    report = []
+    for t in range(1, n_steps + 1):
+        g = _grads(params, 100 + t)
+        gd = _flat_f32(m, g)
+        norm = opt.step(p, gd, t, lr_mults[t - 1])
+        torch.cuda.synchronize()
+        want_norm = oo.step(ocfg, st, g, t, lr_mults[t - 1])
+        got_norm = float(norm.item())
+        assert abs(got_norm - want_norm) <= 1e-5 * want_norm, (got_norm, want_norm)
+        master = opt.master()
+        m1, m2 = opt.moments()
+        for k in params:
+            d_got = master[k].astype(np.float64) - params[k]
+            d_want = st["master"][k] - params[k]
+            e, c = rel_l2(d_got, d_want), cosine(d_got, d_want)
+            report.append((t, k, e, c))
+            if oo.is_adamw_tensor(k):
+                assert e < 1e-5, (t, k, e)
+                assert rel_l2(m1[k], st["m"][k]) < 1e-5, (t, k)
+                assert rel_l2(m2[k], st["v"][k]) < 1e-5, (t, k)
+            else:
+                assert e < ns_tol and c >= 0.999, (t, k, e, c)
+                assert rel_l2(m1[k], st["buf"][k]) < 1e-5, (t, k)
+        # the parameters are the master weights rounded to their type
+        got_p = p.view(torch.int16).cpu().numpy().view(np.uint16) if bf16 else p.cpu().numpy()
+        for name, off, r, c in m.layout:
+            mw = master[name].reshape(-1)
+            if bf16:
+                np.testing.assert_array_equal(got_p[off:off + r * c], bf16_bits(mw))
+            else:
+                np.testing.assert_array_equal(got_p[off:off + r * c], mw)
+    worst = sorted(report, key=lambda x: -x[2])[:4]
+    print(f"[{cfg['name']}] worst weight-change rel-L2: " +
+          ", ".join(f"t{t} {k}: {e:.2e}/cos {c:.6f}" for t, k, e, c in worst))
+
+
+def test_optimizer_steps_fp32():
+    _run_steps(get_config("tiny"), OCFG, 3, [1.0, 0.5, 0.25])
+
+
+def test_optimizer_steps_fp32_no_clip_no_nesterov():
+    _run_steps(get_config("tiny"), {**OCFG, "grad_clip": 0.0, "muon_nesterov": 0,
+                                    "muon_ns_steps": 3}, 2, [1.0, 1.0])
+
+
+@pytest.mark.parametrize("name,over", [
+    ("d20", dict(n_layer=2, seq_len=128, batch=1)),
+    ("gpt2", dict(n_layer=2, seq_len=128, batch=1)),
+])
+def test_optimizer_steps_bf16(name, over):
+    _run_steps(get_config(name, **over), OCFG, 2, [1.0, 0.3])
+
+
+def test_gradient_accumulation_equals_the_batch_gradient():
+    """Two micro-batches of two sequences accumulated with scale 1/2 give the
+    gradient of the four-sequence batch (tiny, fp32, oracle on the batch)."""
+    from dense_gpt_pretraining_amd import Model, binding as b
+    torch = require_gpu()
+    cfg4 = get_config("tiny", batch=4)
+    cfg2 = get_config("tiny", batch=2)
+    params = make_params(cfg4)
+    tokens, targets = make_tokens(cfg4)
+    m = Model(cfg2)
+    p = m.pack(params)
+    acc = torch.full((m.n_params,), float("nan"), dtype=torch.float32, device="cuda")
+    for i, lo in enumerate((0, 2)):
+        _, g = m.forward_backward(p, tokens[lo:lo + 2], targets[lo:lo + 2])
+        b.nc_grad_accumulate(acc.data_ptr(), g.data_ptr(), m.n_params, 0.5, i == 0, m.stream())
+        torch.cuda.synchronize()
+    got = m.unpack(acc)
+    _, want = oracle.forward_backward(cfg4, params, tokens, targets)
+    for k in want:
+        assert rel_l2(got[k], want[k]) < 1e-4, k
+
+
+def test_grad_accumulate_elementwise():
+    from dense_gpt_pretraining_amd import binding as b
+    torch = require_gpu()
+    n = 1000003
+    rng = np.random.default_rng(3)
+    g1 = rng.standard_normal(n).astype(np.float32)
+    g2 = rng.standard_normal(n).astype(np.float32)
+    acc = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+    d1, d2 = torch.from_numpy(g1).cuda(), torch.from_numpy(g2).cuda()
+    s = torch.cuda.current_stream().cuda_stream
+    b.nc_grad_accumulate(acc.data_ptr(), d1.data_ptr(), n, 0.25, 1, s)
+    b.nc_grad_accumulate(acc.data_ptr(), d2.data_ptr(), n, 0.75, 0, s)
+    torch.cuda.synchronize()
+    want = 0.25 * g1.astype(np.float64) + 0.75 * g2.astype(np.float64)
+    assert rel_l2(acc.cpu().numpy(), want) < 1e-7
+
+
+@pytest.mark.timeout(600)
+def test_optimizer_step_at_full_d20_size():
+    """The d20 step in the launch configuration the benchmark times, with
+    its own device-drawn parameters and gradients of a real forward+backward
+    pass; AdamW checked on wte and wlm in full, Muon on the first and last
+    layer's copy of each block matrix (the oracle on each matrix alone)."""
+    from dense_gpt_pretraining_amd import Model, Optimizer
+    torch = require_gpu()
+    cfg = get_config("d20", batch=8)
+    m = Model(cfg)
+    p = m.init_params(cfg["seed_params"])
+    tokens, targets = make_tokens(cfg)
+    _, g = m.forward_backward(p, tokens, targets)
+    torch.cuda.synchronize()
+    params = m.unpack(p)
+    grads = m.unpack(g)
+    del g
+    opt = Optimizer(m, OCFG)
+    opt.init(p)
+    gd = _flat_f32(m, grads)
+    norm = opt.step(p, gd, 1, 1.0)
+    torch.cuda.synchronize()
+    want_norm = oo.global_norm(grads)
+    assert abs(float(norm.item()) - want_norm) <= 1e-5 * want_norm
+    clip = oo.clip_scale(want_norm, OCFG["grad_clip"])
+    master = opt.master()
+    L = cfg["n_layer"]
+    for k in ["wte", "wlm"] + [f"h{l}.{w}" for l in (0, L - 1)
+                               for w in ("wq", "wk", "wv", "wo", "wfc", "wproj")]:
+        g64 = grads[k].astype(np.float64) * clip
+        if oo.is_adamw_tensor(k):
+            want, _, _ = oo.adamw(params[k], g64, 0.0, 0.0, 1, OCFG["adam_lr"], OCFG["adam_beta1"],
+                                  OCFG["adam_beta2"], OCFG["adam_eps"],
+                                  OCFG["adam_weight_decay"])
+            tol, cmin = 1e-5, 0.99999
+        else:
+            want, _ = oo.muon(params[k], g64, 0.0, OCFG["muon_lr"], OCFG["muon_momentum"], True,
+                              OCFG["muon_ns_steps"], OCFG["muon_weight_decay"])
+            tol, cmin = 3e-2, 0.999
+        d_got = master[k].astype(np.float64) - params[k]
+        d_want = want - params[k]
+        e, c = rel_l2(d_got, d_want), cosine(d_got, d_want)
+        print(f"[d20 full] {k}: weight change rel-L2 {e:.2e} cos {c:.6f}")
+        assert e < tol and c >= cmin, (k, e, c)
