@@ -55,6 +55,16 @@ class nc_tensor_info(C.Structure):
 
 
 def _load():
+    # PyTorch ships its own HIP runtime (libamdhip64, libhsa-runtime64) under
+    # the same soname as the system one libnc.so is linked against.  Loading
+    # torch first makes the dynamic loader bind libnc.so to torch's copy, so
+    # the process drives the GPU through one runtime; loading libnc.so first
+    # would map both runtimes into the process, with two instances of the
+    # runtime's state for one device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m dense_gpt_pretraining_amd.build` "
@@ -75,6 +85,9 @@ _sigs = {
                                         C.c_size_t, _P]),
     "nc_forward_backward": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
                                       C.c_size_t, _P]),
+    "nc_workspace_size_recompute": (C.c_int, [C.POINTER(nc_config), C.POINTER(C.c_size_t)]),
+    "nc_forward_backward_recompute": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
+                                                C.c_size_t, _P]),
     "nc_forward_backward_timed": (C.c_int, [C.POINTER(nc_config), _P, _P, _P, _P, _P, _P,
                                             C.c_size_t, _P, C.POINTER(nc_kernel_stat),
                                             C.c_int32, C.POINTER(C.c_int32)]),
@@ -167,6 +180,19 @@ def nc_forward_token_loss(cfg, params, tokens, targets, loss, token_loss, ws, ws
 
 def nc_forward_backward(cfg, params, tokens, targets, loss, grads, ws, ws_bytes, stream):
     _check("nc_forward_backward", _lib.nc_forward_backward(
+        C.byref(cfg), params, tokens, targets, loss, grads, ws, ws_bytes, stream))
+
+
+def nc_workspace_size_recompute(cfg: nc_config) -> int:
+    b = C.c_size_t()
+    _check("nc_workspace_size_recompute", _lib.nc_workspace_size_recompute(C.byref(cfg),
+                                                                           C.byref(b)))
+    return b.value
+
+
+def nc_forward_backward_recompute(cfg, params, tokens, targets, loss, grads, ws, ws_bytes,
+                                  stream):
+    _check("nc_forward_backward_recompute", _lib.nc_forward_backward_recompute(
         C.byref(cfg), params, tokens, targets, loss, grads, ws, ws_bytes, stream))
 
 
@@ -327,13 +353,17 @@ class Model:
             host = flat.float().cpu().numpy()
         return {name: host[off:off + r * c].reshape(r, c) for name, off, r, c in self.layout}
 
-    def workspace(self, with_backward: bool):
-        key = bool(with_backward)
+    def workspace(self, with_backward: bool, recompute: bool = False):
+        key = ("recompute" if recompute else bool(with_backward))
         if key not in self._ws:
-            n = nc_workspace_size(self.c, key)
+            n = (nc_workspace_size_recompute(self.c) if recompute
+                 else nc_workspace_size(self.c, bool(with_backward)))
             self._ws[key] = self.torch.empty(max(n, 256), dtype=self.torch.uint8,
                                              device=self.device)
         return self._ws[key]
+
+    def free_workspaces(self):
+        self._ws = {}
 
     def init_params(self, seed: int):
         p = self.torch.empty(self.n_params, dtype=self.tdtype, device=self.device)
@@ -361,16 +391,16 @@ class Model:
                               self.stream())
         return loss, tl
 
-    def forward_backward(self, params, tokens, targets, grads=None):
+    def forward_backward(self, params, tokens, targets, grads=None, recompute: bool = False):
         torch = self.torch
         tok, tgt = self._tok(tokens), self._tok(targets)
         loss = torch.empty(1, dtype=torch.float32, device=self.device)
         if grads is None:
             grads = torch.empty(self.n_params, dtype=torch.float32, device=self.device)
-        ws = self.workspace(True)
-        nc_forward_backward(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(),
-                            loss.data_ptr(), grads.data_ptr(), ws.data_ptr(), ws.numel(),
-                            self.stream())
+        ws = self.workspace(True, recompute)
+        fn = nc_forward_backward_recompute if recompute else nc_forward_backward
+        fn(self.c, params.data_ptr(), tok.data_ptr(), tgt.data_ptr(), loss.data_ptr(),
+           grads.data_ptr(), ws.data_ptr(), ws.numel(), self.stream())
         return loss, grads
 
 

@@ -164,6 +164,15 @@ hipError_t init_normal(T* p, int64_t n, float std, uint64_t seed,
                        uint64_t stream_id, hipStream_t s);
 template <typename T>
 hipError_t zero_elems(T* p, int64_t n, hipStream_t s);
+// The stream of an entry point whose host-side checks have passed.  HIP keeps
+// one "last error" per host thread, and a failed HIP call made earlier on the
+// thread by the caller (or by a framework it uses) leaves it set; it is
+// dropped here, before the entry point's first launch, so that the
+// hipGetLastError checks after its launches report only its own errors.
+inline hipStream_t enqueue_stream(void* stream) {
+    (void)hipGetLastError();
+    return static_cast<hipStream_t>(stream);
+}
 // records the HIP error behind an NC_ERR_HIP return (read by nc_last_hip_error)
 void note_hip_error(int err);
 

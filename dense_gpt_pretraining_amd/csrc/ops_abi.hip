@@ -28,7 +28,7 @@ int nc_op_matmul(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
     if (ldc < N) return NC_ERR_CONFIG;
     if (a_kmajor ? lda < K : lda < M) return NC_ERR_CONFIG;
     if (b_kmajor ? ldb < K : ldb < N) return NC_ERR_CONFIG;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     nc::Epilogue e;
     e.mode = nc::EPI_STORE_F32;
     if (dtype == NC_F32)
@@ -63,7 +63,7 @@ int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
     if (rc != NC_OK) return rc;
     if (!q || !k || !v || !o || !lse) return NC_ERR_NULL;
     if (!al16(q) || !al16(k) || !al16(v) || !al16(o) || !al16(lse)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     if (dtype == NC_F32)
         return ret(nc::attn_fwd<float>(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), ldq, ldkv,
@@ -85,7 +85,7 @@ int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
         !al16(scratch) || !al16(dq) || !al16(dk) || !al16(dv))
         return NC_ERR_ALIGN;
     if (scratch_bytes < nc::attn_bwd_scratch_bytes(B, T, H, hd)) return NC_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     float* sc = static_cast<float*>(scratch);
     if (dtype == NC_F32)
         return ret(nc::attn_bwd<float>(static_cast<const float*>(q), static_cast<const float*>(k),
@@ -118,7 +118,7 @@ int nc_op_softcap_ce(int32_t dtype, int32_t N, int32_t V, int64_t ldz, void* z,
     if (!z || !targets || !tok_loss || (want_grad && !rowscale)) return NC_ERR_NULL;
     if (!al16(z) || !al16(targets) || !al16(tok_loss) || (rowscale && !al16(rowscale)))
         return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     if (dtype == NC_F32)
         return ret(nc::softcap_ce<float>(static_cast<float*>(z), ldz, V, N, targets, softcap,
                                          rowscale, inv_n, tok_loss, want_grad != 0, s));
@@ -133,7 +133,7 @@ int nc_op_rope_qknorm_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_
     if (hd != 64 && hd != 128) return NC_ERR_UNSUPPORTED;
     if (!qkv || !rqk || !tables) return NC_ERR_NULL;
     if (!al16(qkv) || !al16(rqk) || !al16(tables)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     float* cos_t = tables;
     float* sin_t = tables + (int64_t)T * (hd / 2);
     hipError_t e = nc::rope_tables(T, hd, base, cos_t, sin_t, s);

@@ -524,7 +524,7 @@ int nc_optim_init(const nc_config* cfg, const void* params, void* state, void* s
     if (rc != NC_OK) return rc;
     if (!params || !state) return NC_ERR_NULL;
     if (!nc::al(params, 256) || !nc::al(state, 256)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     const size_t arr = nc::al256((size_t)n * 4);
     float* master = static_cast<float*>(state);
     float* s1 = reinterpret_cast<float*>(static_cast<char*>(state) + arr);
@@ -559,7 +559,7 @@ int nc_optim_step(const nc_config* cfg, const nc_optim_config* ocfg, int64_t ste
         !nc::al(ws, 256) || (grad_norm && !nc::al(grad_norm, 4)))
         return NC_ERR_ALIGN;
     if (ws_bytes < p.bytes) return NC_ERR_WORKSPACE;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     if (cfg->dtype == NC_BF16)
         return nc::optim_step<nc::bf16_t>(cfg, ocfg, step, lr_mult, grads, params, state,
                                           grad_norm, static_cast<char*>(ws), p, s);
@@ -573,7 +573,7 @@ int nc_grad_accumulate(float* acc, const float* grads, int64_t n, float scale, i
     if (n < 0 || !std::isfinite(scale)) return NC_ERR_CONFIG;
     if (!nc::al(acc, 16) || !nc::al(grads, 16)) return NC_ERR_ALIGN;
     if (n == 0) return NC_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     const unsigned grid = (unsigned)std::max<int64_t>(
         1, std::min<int64_t>(nc::ceil_div(n / 4, nc::kOptThreads), 65536));
     hipLaunchKernelGGL(nc::k_grad_accumulate, dim3(grid), dim3(nc::kOptThreads), 0, s, acc, grads,

@@ -104,8 +104,10 @@ struct Plan {
     size_t cos_t, sin_t, r0, x, r1, qkv, rqk, o, lse, xm, r2, g, rf, z, tok_loss, loss_tmp;
     size_t dres, dres_t, dn, dgu, dout, delta, dq, dk, dv, dqkv, wt, splitk, embed;
     size_t splitk_bytes = 0, embed_bytes = 0;
-    int slots = 1;     // saved-activation slots per layer tensor (L with backward, 1 without)
+    int slots = 1;     // saved-activation slots per layer tensor (L with backward, 1 without
+                       // or with recompute)
     int x_slots = 2;   // block inputs: L+1 with backward, 2 (ping-pong) without
+    bool recompute = false;   // the backward forms each block's tensors again
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -118,15 +120,16 @@ hipError_t gemm_w(int M, int N, int K, const T* A, int64_t lda, const T* W, int6
     return nc::gemm<T>(M, N, K, A, lda, true, W, ldw, false, C, ldc, e, nullptr, 0, s);
 }
 
-Plan make_plan(const nc_config& c, bool bwd) {
+Plan make_plan(const nc_config& c, bool bwd, bool recompute = false) {
     Plan p;
+    p.recompute = bwd && recompute;
     const int64_t N = (int64_t)c.batch * c.seq_len;
     const int64_t D = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_mlp, V = c.vocab;
     const int64_t Vp = vocab_pad(c);
     const int64_t Wq = (H + 2) * hd;
     const size_t es = c.dtype == NC_BF16 ? 2 : 4;
     const int L = c.n_layer;
-    p.slots = bwd ? L : 1;
+    p.slots = bwd && !p.recompute ? L : 1;
     p.x_slots = bwd ? L + 1 : 2;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t r = off; off += align256(bytes); return r; };
@@ -302,6 +305,62 @@ struct Step {
     // causal score pairs of one head over the batch: B * T(T+1)/2
     double pairs() const { return (double)c.batch * c.seq_len * (c.seq_len + 1) / 2.0; }
 
+    // One block's forward from its input x: saves (into slot sl) everything
+    // its backward reads; with_proj also forms the block output xn (the
+    // recompute pass before a block's backward needs everything but xn).
+    int layer_fwd(int l, int sl, T* x, T* xn, bool with_proj) {
+        const float eps = c.rms_eps;
+        float* cos_t = at<float>(p.cos_t);
+        float* sin_t = at<float>(p.sin_t);
+        const double rowb = (double)N * D * es();
+        float* r1 = R1(sl);
+        T* qkv = QKV(sl);
+        NC_RUN("rms_stats", 0, rowb + N * 4.0, nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
+        if constexpr (std::is_same<T, nc::bf16_t>::value) {
+            // rotary + QK-norm in the projection's epilogue
+            nc::Epilogue e = epi(nc::EPI_QKV_ROPE, r1);
+            e.cos_t = cos_t;
+            e.sin_t = sin_t;
+            e.rqk = RQK(sl);
+            e.seq_len = c.seq_len;
+            e.n_head = (int)H;
+            e.head_dim = (int)hd;
+            e.eps = eps;
+            NC_RUN("gemm_nt_qkv_rope", gf(N, Wq, D), gb(N, Wq, D, es(), N * (H + 5.0) * 4.0),
+                   nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
+                               Wq, e, nullptr, 0, s));
+        } else {
+            NC_RUN("gemm_nt_rowscale", gf(N, Wq, D), gb(N, Wq, D, es(), N * 4.0),
+                   nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true, qkv,
+                               Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
+            NC_RUN("rope_qknorm_fwd", 0, 2.0 * N * (H + 1) * hd * es() + N * (H + 1) * 4.0,
+                   nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t, sin_t,
+                                          eps, RQK(sl), s));
+        }
+        NC_RUN("attn_fwd", 4.0 * hd * H * pairs(),
+               2.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 4.0,
+               nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
+                               c.batch, c.seq_len, (int)H, (int)hd, s));
+        T* xm = XM(sl);
+        NC_RUN("gemm_nt_resid", gf(N, D, H * hd), gb(N, D, H * hd, es(), rowb),
+               nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true, W(i_layer(l, 3)),
+                           H * hd, true, xm, D, epi(nc::EPI_RESID, nullptr, x), nullptr, 0, s));
+        float* r2 = R2(sl);
+        NC_RUN("rms_stats", 0, rowb + N * 4.0, nc::rms_stats<T>(xm, (int)N, (int)D, eps, r2, s));
+        NC_RUN("gemm_nt_relu2", gf(N, F, D), gb(N, F, D, es(), N * 4.0),
+               nc::gemm<T>((int)N, (int)F, (int)D, xm, D, true, W(i_layer(l, 4)), D, true, G(sl),
+                           F, epi(nc::EPI_ROWSCALE_RELU2, r2), nullptr, 0, s));
+        if (with_proj)
+            NC_RUN("gemm_nt_resid", gf(N, D, F), gb(N, D, F, es(), rowb),
+                   nc::gemm<T>((int)N, (int)D, (int)F, G(sl), F, true, W(i_layer(l, 5)), F, true,
+                               xn, D, epi(nc::EPI_RESID, nullptr, xm), nullptr, 0, s));
+        return NC_OK;
+    }
+
+    // slot of layer l's saved tensors: one per layer when the backward keeps
+    // them all, a single one without backward or with recompute
+    int slot_of(int l) const { return p.slots > 1 ? l : 0; }
+
     int forward(const int32_t* tok, const int32_t* tgt, float* loss, float* tok_loss, bool bwd) {
         const float eps = c.rms_eps;
         float* cos_t = at<float>(p.cos_t);
@@ -313,52 +372,12 @@ struct Step {
                nc::embed_fwd<T>(W(i_wte()), tok, (int)N, (int)D, eps, X(0), at<float>(p.r0), s));
         const int L = c.n_layer;
         for (int l = 0; l < L; ++l) {
-            const int sl = bwd ? l : 0;
+            // with backward every block input is kept (L+1 slots); without,
+            // two slots alternate
             T* x = X(bwd ? l : (l & 1));
             T* xn = X(bwd ? l + 1 : ((l + 1) & 1));
-            float* r1 = R1(sl);
-            T* qkv = QKV(sl);
-            NC_RUN("rms_stats", 0, rowb + N * 4.0,
-                   nc::rms_stats<T>(x, (int)N, (int)D, eps, r1, s));
-            if constexpr (std::is_same<T, nc::bf16_t>::value) {
-                // rotary + QK-norm in the projection's epilogue
-                nc::Epilogue e = epi(nc::EPI_QKV_ROPE, r1);
-                e.cos_t = cos_t;
-                e.sin_t = sin_t;
-                e.rqk = RQK(sl);
-                e.seq_len = c.seq_len;
-                e.n_head = (int)H;
-                e.head_dim = (int)hd;
-                e.eps = eps;
-                NC_RUN("gemm_nt_qkv_rope", gf(N, Wq, D), gb(N, Wq, D, es(), N * (H + 5.0) * 4.0),
-                       nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true,
-                                   qkv, Wq, e, nullptr, 0, s));
-            } else {
-                NC_RUN("gemm_nt_rowscale", gf(N, Wq, D), gb(N, Wq, D, es(), N * 4.0),
-                       nc::gemm<T>((int)N, (int)Wq, (int)D, x, D, true, W(i_layer(l, 0)), D, true,
-                                   qkv, Wq, epi(nc::EPI_ROWSCALE, r1), nullptr, 0, s));
-                NC_RUN("rope_qknorm_fwd", 0, 2.0 * N * (H + 1) * hd * es() + N * (H + 1) * 4.0,
-                       nc::rope_qknorm_fwd<T>(qkv, (int)N, c.seq_len, (int)H, (int)hd, cos_t,
-                                              sin_t, eps, RQK(sl), s));
-            }
-            NC_RUN("attn_fwd", 4.0 * hd * H * pairs(),
-                   2.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 4.0,
-                   nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
-                                   c.batch, c.seq_len, (int)H, (int)hd, s));
-            T* xm = XM(sl);
-            NC_RUN("gemm_nt_resid", gf(N, D, H * hd), gb(N, D, H * hd, es(), rowb),
-                   nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true,
-                               W(i_layer(l, 3)), H * hd, true, xm, D,
-                               epi(nc::EPI_RESID, nullptr, x), nullptr, 0, s));
-            float* r2 = R2(sl);
-            NC_RUN("rms_stats", 0, rowb + N * 4.0,
-                   nc::rms_stats<T>(xm, (int)N, (int)D, eps, r2, s));
-            NC_RUN("gemm_nt_relu2", gf(N, F, D), gb(N, F, D, es(), N * 4.0),
-                   nc::gemm<T>((int)N, (int)F, (int)D, xm, D, true, W(i_layer(l, 4)), D, true,
-                               G(sl), F, epi(nc::EPI_ROWSCALE_RELU2, r2), nullptr, 0, s));
-            NC_RUN("gemm_nt_resid", gf(N, D, F), gb(N, D, F, es(), rowb),
-                   nc::gemm<T>((int)N, (int)D, (int)F, G(sl), F, true, W(i_layer(l, 5)), F, true,
-                               xn, D, epi(nc::EPI_RESID, nullptr, xm), nullptr, 0, s));
+            int rc = layer_fwd(l, slot_of(l), x, xn, true);
+            if (rc != NC_OK) return rc;
         }
         T* hL = X(bwd ? L : (L & 1));
         float* rf = at<float>(p.rf);
@@ -415,13 +434,20 @@ struct Step {
         const float* sin_t = at<float>(p.sin_t);
         for (int l = L - 1; l >= 0; --l) {
             T* x = X(l);
-            T* xm = XM(l);
+            if (p.recompute && l < L - 1) {
+                // the block's saved tensors were overwritten by later blocks:
+                // form them again from its input (same kernels, same bits)
+                int rc = layer_fwd(l, slot_of(l), x, nullptr, false);
+                if (rc != NC_OK) return rc;
+            }
+            const int sl = slot_of(l);
+            T* xm = XM(sl);
             // MLP: x_{l+1} = xm + relu(r2 xm W_fc^T)^2 W_proj^T
             NC_RUN("gemm_nt_relu2_bwd", gf(N, F, D), gb(N, F, D, es(), N * F * es() + N * 4.0),
                    gemm_w<T>((int)N, (int)F, (int)D, dres_t, D, W(i_layer(l, 5)), F, dgu, F,
-                             epi(nc::EPI_RELU2_BWD, R2(l), G(l)), s));
+                             epi(nc::EPI_RELU2_BWD, R2(sl), G(sl)), s));
             NC_RUN("gemm_tn_f32", gf(D, F, N), gb(D, F, N, 4.0),
-                   nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(l), F, false,
+                   nc::gemm<T>((int)D, (int)F, (int)N, dres_t, D, false, G(sl), F, false,
                                G_of(i_layer(l, 5)), F, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("gemm_nt_dn", gf(N, D, F), gb(N, D, F, es()),
                    gemm_w<T>((int)N, (int)D, (int)F, dgu, F, W(i_layer(l, 4)), D, dn, D,
@@ -430,23 +456,23 @@ struct Step {
                    nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
                                G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("norm_bwd_resid", 0, nbb,
-                   nc::norm_bwd_resid<T>(dn, xm, R2(l), (int)N, (int)D, dres, dres_t, s));
+                   nc::norm_bwd_resid<T>(dn, xm, R2(sl), (int)N, (int)D, dres, dres_t, s));
             // attention: xm = x + o W_o^T
             NC_RUN("gemm_nt_store", gf(N, H * hd, D), gb(N, H * hd, D, es()),
                    gemm_w<T>((int)N, (int)(H * hd), (int)D, dres_t, D, W(i_layer(l, 3)), H * hd,
                              dout, H * hd, epi(nc::EPI_STORE_T), s));
             NC_RUN("gemm_tn_f32", gf(D, H * hd, N), gb(D, H * hd, N, 4.0),
-                   nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(l), H * hd,
+                   nc::gemm<T>((int)D, (int)(H * hd), (int)N, dres_t, D, false, O(sl), H * hd,
                                false, G_of(i_layer(l, 3)), H * hd, epi(nc::EPI_STORE_F32), sk, skb,
                                s));
-            T* qkv = QKV(l);
+            T* qkv = QKV(sl);
             if constexpr (std::is_same<T, nc::bf16_t>::value) {
                 // QK-norm and rotary backward fused into the attention kernels,
                 // which write the bf16 dqkv directly
                 nc::AttnBwdFuse fz;
                 fz.y = reinterpret_cast<const nc::bf16_t*>(qkv);
-                fz.rqk = RQK(l);
-                fz.r1 = R1(l);
+                fz.rqk = RQK(sl);
+                fz.r1 = R1(sl);
                 fz.cos_t = cos_t;
                 fz.sin_t = sin_t;
                 fz.dqkv = reinterpret_cast<nc::bf16_t*>(dqkv);
@@ -455,21 +481,21 @@ struct Step {
                        4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
                            N * (H + 2) * hd * es(),
                        nc::attn_bwd_mfma(qb, qb + H * hd, qb + (H + 1) * hd, Wq, Wq,
-                                         reinterpret_cast<const nc::bf16_t*>(O(l)),
-                                         reinterpret_cast<const nc::bf16_t*>(dout), LSE(l),
+                                         reinterpret_cast<const nc::bf16_t*>(O(sl)),
+                                         reinterpret_cast<const nc::bf16_t*>(dout), LSE(sl),
                                          at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
                                          (int)H, (int)hd, s, &fz));
             } else {
                 NC_RUN("attn_bwd", 8.0 * hd * H * pairs(),
                        4.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 8.0 +
                            4.0 * N * (H + 2) * hd,
-                       nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(l), dout,
-                                       LSE(l), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
+                       nc::attn_bwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), dout,
+                                       LSE(sl), at<float>(p.delta), dq, dk, dv, c.batch, c.seq_len,
                                        (int)H, (int)hd, s));
                 NC_RUN("rope_qknorm_bwd", 0,
                        N * (H + 1) * hd * es() + 4.0 * N * (H + 2) * hd + N * (H + 2) * hd * es() +
                            N * (H + 2) * 4.0,
-                       nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(l), R1(l), (int)N, c.seq_len,
+                       nc::rope_qknorm_bwd<T>(qkv, dq, dk, dv, RQK(sl), R1(sl), (int)N, c.seq_len,
                                               (int)H, (int)hd, cos_t, sin_t, dqkv, s));
             }
             NC_RUN("gemm_nt_dn", gf(N, D, Wq), gb(N, D, Wq, es()),
@@ -479,7 +505,7 @@ struct Step {
                    nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
                                G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("norm_bwd_resid", 0, nbb,
-                   nc::norm_bwd_resid<T>(dn, x, R1(l), (int)N, (int)D, dres, dres_t, s));
+                   nc::norm_bwd_resid<T>(dn, x, R1(sl), (int)N, (int)D, dres, dres_t, s));
         }
         // embedding: h0 = r0 e, e = W_te[tok]
         float* de = at<float>(p.dn);
@@ -496,9 +522,9 @@ struct Step {
 template <typename T>
 int run_step(const nc_config& c, const void* params, const int32_t* tok, const int32_t* tgt,
              float* loss, float* tok_loss, float* grads, void* ws, size_t ws_bytes,
-             hipStream_t s, Prof* prof = nullptr) {
+             hipStream_t s, Prof* prof = nullptr, bool recompute = false) {
     const bool bwd = grads != nullptr;
-    Plan p = make_plan(c, bwd);
+    Plan p = make_plan(c, bwd, recompute);
     if (ws_bytes < p.bytes) return NC_ERR_WORKSPACE;
     Step<T> st(c, p, ws, s, params, prof);
     int rc = st.forward(tok, tgt, loss, tok_loss, bwd);
@@ -578,7 +604,7 @@ int nc_init_params(const nc_config* cfg, uint64_t seed, void* params, void* stre
     if (rc != NC_OK) return rc;
     if (!params) return NC_ERR_NULL;
     if (!aligned(params, 256)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     int64_t total = 0;
     std::vector<TensorDesc> lay = layout(*cfg, &total);
     const bool bf = cfg->dtype == NC_BF16;
@@ -611,7 +637,7 @@ int nc_forward_token_loss(const nc_config* cfg, const void* params, const int32_
                           size_t ws_bytes, void* stream) {
     int rc = check_common(cfg, params, tokens, targets, loss, token_loss, ws);
     if (rc != NC_OK) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     if (cfg->dtype == NC_BF16)
         return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, token_loss, nullptr, ws,
                                     ws_bytes, s);
@@ -626,11 +652,34 @@ int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t*
     if (rc != NC_OK) return rc;
     if (!grads) return NC_ERR_NULL;
     if (!aligned(grads, 256)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     if (cfg->dtype == NC_BF16)
         return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, nullptr, grads, ws,
                                     ws_bytes, s);
     return run_step<float>(*cfg, params, tokens, targets, loss, nullptr, grads, ws, ws_bytes, s);
+}
+
+int nc_workspace_size_recompute(const nc_config* cfg, size_t* bytes) {
+    int rc = validate(cfg);
+    if (rc != NC_OK) return rc;
+    if (!bytes) return NC_ERR_NULL;
+    *bytes = make_plan(*cfg, true, true).bytes;
+    return NC_OK;
+}
+
+int nc_forward_backward_recompute(const nc_config* cfg, const void* params,
+                                  const int32_t* tokens, const int32_t* targets, float* loss,
+                                  float* grads, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_common(cfg, params, tokens, targets, loss, nullptr, ws);
+    if (rc != NC_OK) return rc;
+    if (!grads) return NC_ERR_NULL;
+    if (!aligned(grads, 256)) return NC_ERR_ALIGN;
+    hipStream_t s = nc::enqueue_stream(stream);
+    if (cfg->dtype == NC_BF16)
+        return run_step<nc::bf16_t>(*cfg, params, tokens, targets, loss, nullptr, grads, ws,
+                                    ws_bytes, s, nullptr, true);
+    return run_step<float>(*cfg, params, tokens, targets, loss, nullptr, grads, ws, ws_bytes, s,
+                           nullptr, true);
 }
 
 int nc_forward_backward_timed(const nc_config* cfg, const void* params, const int32_t* tokens,
@@ -641,7 +690,7 @@ int nc_forward_backward_timed(const nc_config* cfg, const void* params, const in
     if (rc != NC_OK) return rc;
     if (!grads || !n_out || (cap > 0 && !stats)) return NC_ERR_NULL;
     if (!aligned(grads, 256)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     Prof prof;
     prof.s = s;
     g_prof = &prof;
@@ -682,7 +731,7 @@ int nc_validate_tokens(const nc_config* cfg, const int32_t* tokens, const int32_
     if (rc != NC_OK) return rc;
     if (!tokens || !targets || !n_bad) return NC_ERR_NULL;
     if (!aligned(tokens, 4) || !aligned(targets, 4) || !aligned(n_bad, 4)) return NC_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s = nc::enqueue_stream(stream);
     NC_TRY(nc::zero_elems<int32_t>(n_bad, 1, s));
     NC_TRY(nc::count_bad_ids(tokens, targets, (int64_t)cfg->batch * cfg->seq_len, cfg->vocab,
                              n_bad, s));

@@ -161,6 +161,24 @@ int nc_forward_backward(const nc_config* cfg, const void* params,
                         float* loss, float* grads, void* ws, size_t ws_bytes,
                         void* stream);
 
+/*
+ * Activation recompute (the llm.c article on qian.cx names it among its
+ * training options): the same step as nc_forward_backward with a workspace
+ * that keeps only the block inputs of every layer plus one layer's other
+ * saved tensors; before each block's backward pass the block's forward is run
+ * again from its input (everything but the block output).  That costs about
+ * one more forward pass of the blocks and cuts the workspace by the other
+ * per-layer tensors (about 23 GB of the d20 step's 60 GB), so longer
+ * sequences or larger batches fit.  The kernels are the step's own and
+ * deterministic, so loss and gradients are bitwise those of
+ * nc_forward_backward.  ws_bytes >= nc_workspace_size_recompute(cfg).
+ */
+int nc_workspace_size_recompute(const nc_config* cfg, size_t* bytes);
+int nc_forward_backward_recompute(const nc_config* cfg, const void* params,
+                                  const int32_t* tokens, const int32_t* targets,
+                                  float* loss, float* grads, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* per-kernel account of one step (nc_forward_backward_timed) */
 typedef struct nc_kernel_stat {
     char name[48];      /* kernel label, e.g. "gemm_nt_relu2" */
