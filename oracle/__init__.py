@@ -9,6 +9,7 @@ from .model import (
     causal_mqa_attention,
     causal_mqa_attention_backward,
     forward_backward,
+    forward_logits,
     forward_loss,
     rms_norm,
     rms_norm_backward,
@@ -21,7 +22,7 @@ from .model import (
 
 __all__ = [
     "causal_mqa_attention", "causal_mqa_attention_backward",
-    "forward_backward", "forward_loss", "rms_norm", "rms_norm_backward",
+    "forward_backward", "forward_logits", "forward_loss", "rms_norm", "rms_norm_backward",
     "rotary", "rotary_backward", "rotary_tables", "softcap",
     "softcap_cross_entropy",
 ]

@@ -367,3 +367,24 @@ def forward_backward(cfg: dict, params: dict, tokens: np.ndarray,
     np.add.at(dwte, tokens.reshape(-1), de.reshape(-1, de.shape[-1]))
     grads["wte"] = dwte
     return float(np.mean(tok_loss)), grads
+
+
+def forward_logits(cfg: dict, params: dict, tokens: np.ndarray, positions=None):
+    """Softcapped logits c = s*tanh(z/s) of every sequence at the given
+    positions (all positions if None): [B, P, V] float64.
+
+    This is what generation reads: the next-token distribution at position t
+    is softmax(c_t).  It is the forward pass of forward_loss without the
+    cross-entropy; causality makes c_t a function of tokens[:, :t+1] alone,
+    which is what an inference engine with a key/value cache computes one
+    position at a time (inference feature of the nanochat pages: a KV cache
+    with prefill and decode)."""
+    B, T = tokens.shape
+    cos, sin = rotary_tables(T, cfg["head_dim"], cfg["rope_base"])
+    _, h, _ = _embed(cfg, params, tokens)
+    for layer in range(cfg["n_layer"]):
+        h, _ = _block_forward(cfg, params, layer, h, cos, sin)
+    pos = np.arange(T) if positions is None else np.asarray(positions)
+    f, _ = rms_norm(h[:, pos, :], cfg["rms_eps"])
+    z = f @ _w(params, "wlm").T
+    return softcap(z, cfg["softcap"])

@@ -7,9 +7,12 @@ Bars, from the arithmetic of each part:
   the gradient norm within 1e-5 relative L2;
 * Muon's Newton-Schulz iteration runs in fp32 for the fp32 configuration
   (weight change within 1e-4 relative L2) and on bf16 matrix cores for the
-  bf16 ones, where each stored matrix is rounded to bf16: the weight change
-  of each Muon tensor within 3e-2 relative L2 with cosine >= 0.999 (the bf16
-  bar of the step's gradients);
+  bf16 ones, where each stored matrix is rounded to bf16: on random
+  gradients the weight change of each Muon tensor within 3e-2 relative L2
+  with cosine >= 0.999 (the bf16 bar of the step's gradients); on the real
+  gradients of the full-size test, whose small singular values the iteration
+  amplifies, within twice the departure of a float64 iteration that rounds
+  the same matrices to bf16 (and never looser than needed for 3e-2);
 * the parameters written are the fp32 master weights rounded to the
   parameter type (round to nearest even), bit for bit.
 """
@@ -187,9 +190,45 @@ def test_optimizer_step_at_full_d20_size():
         else:
             want, _ = oo.muon(params[k], g64, 0.0, OCFG["muon_lr"], OCFG["muon_momentum"], True,
                               OCFG["muon_ns_steps"], OCFG["muon_weight_decay"])
-            tol, cmin = 3e-2, 0.999
+            # the bf16 iteration departs from the float64 one by an amount
+            # the gradient's spectrum decides (small singular values pass
+            # through a map of slope up to 3.4445^5); bound it by twice the
+            # departure of the same iteration with its matrices rounded to
+            # bf16 where the GPU stores them
+            emu = _muon_bf16_rounded(params[k], g64)
+            e_emu = rel_l2(emu - params[k], want - params[k])
+            c_emu = cosine(emu - params[k], want - params[k])
+            tol = max(3e-2, 2 * e_emu)
+            cmin = min(0.999, 1 - 2 * (1 - c_emu))
         d_got = master[k].astype(np.float64) - params[k]
         d_want = want - params[k]
         e, c = rel_l2(d_got, d_want), cosine(d_got, d_want)
-        print(f"[d20 full] {k}: weight change rel-L2 {e:.2e} cos {c:.6f}")
+        print(f"[d20 full] {k}: weight change rel-L2 {e:.2e} cos {c:.6f} (bar {tol:.2e} / "
+              f"{cmin:.6f})")
         assert e < tol and c >= cmin, (k, e, c)
+
+
+def _muon_bf16_rounded(theta, g):
+    """Muon's first step (no momentum history, Nesterov) with the iteration's
+    stored matrices (X0, the Gram matrix, b A + c A^2, each new X) rounded to
+    bf16 and every product accumulated in float64: the rounding the GPU
+    applies, without its accumulation order."""
+    from nc_synth import bf16_round
+
+    def r(x):
+        return bf16_round(np.asarray(x, np.float32)).astype(np.float64)
+
+    a, b, c = oo.NS_COEFFS
+    mu = OCFG["muon_momentum"]
+    u = g + mu * g
+    X = u / (np.linalg.norm(u) + 1e-7)
+    tall = X.shape[0] > X.shape[1]
+    X = r(X.T if tall else X)
+    for _ in range(OCFG["muon_ns_steps"]):
+        A = r(X @ X.T)
+        B = r(b * A + c * (A @ A))
+        X = r(a * X + B @ X)
+    X = X.T if tall else X
+    rows, cols = theta.shape
+    lr = OCFG["muon_lr"]
+    return theta * (1 - lr * OCFG["muon_weight_decay"]) - lr * np.sqrt(max(1.0, rows / cols)) * X
