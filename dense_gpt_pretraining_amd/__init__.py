@@ -14,7 +14,7 @@ _EXPORTS = (
     "nc_forward_token_loss", "nc_init_params", "nc_last_hip_error", "nc_param_count",
     "nc_param_layout", "nc_status_string", "nc_validate_tokens", "nc_workspace_size",
     "NC_BF16", "NC_F32", "Optimizer", "make_optim_config", "nc_optim_step", "nc_optim_init",
-    "nc_grad_accumulate", "nc_lr_multiplier",
+    "nc_grad_accumulate", "nc_lr_multiplier", "Generator", "nc_prefill", "nc_decode_step",
 )
 
 __all__ = list(_EXPORTS)

@@ -101,6 +101,13 @@ _sigs = {
                                 C.c_float, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "nc_grad_accumulate": (C.c_int, [_P, _P, C.c_int64, C.c_float, C.c_int32, _P]),
     "nc_lr_multiplier": (C.c_double, [C.c_int64, C.c_int64, C.c_int64, C.c_double]),
+    "nc_kv_cache_size": (C.c_int, [C.POINTER(nc_config), C.c_int32, C.POINTER(C.c_size_t)]),
+    "nc_infer_workspace_size": (C.c_int, [C.POINTER(nc_config), C.c_int32, C.c_int32,
+                                          C.POINTER(C.c_size_t)]),
+    "nc_prefill": (C.c_int, [C.POINTER(nc_config), _P, _P, C.c_int32, C.c_int32, _P, _P, _P,
+                             C.c_size_t, _P]),
+    "nc_decode_step": (C.c_int, [C.POINTER(nc_config), _P, _P, C.c_int32, C.c_int32, _P, _P, _P,
+                                 C.c_size_t, _P]),
     "nc_op_matmul": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
                                C.c_int32, _P, C.c_int64, C.c_int32, _P, C.c_int64, _P,
                                C.c_size_t, _P]),
@@ -254,6 +261,29 @@ def nc_lr_multiplier(step: int, total: int, warmup: int, final_frac: float) -> f
     if v < 0:
         raise NcError("nc_lr_multiplier", -2, "a schedule argument is out of range")
     return v
+
+
+def nc_kv_cache_size(cfg: nc_config, max_seq: int) -> int:
+    b = C.c_size_t()
+    _check("nc_kv_cache_size", _lib.nc_kv_cache_size(C.byref(cfg), max_seq, C.byref(b)))
+    return b.value
+
+
+def nc_infer_workspace_size(cfg: nc_config, max_seq: int, t0: int) -> int:
+    b = C.c_size_t()
+    _check("nc_infer_workspace_size", _lib.nc_infer_workspace_size(C.byref(cfg), max_seq, t0,
+                                                                   C.byref(b)))
+    return b.value
+
+
+def nc_prefill(cfg, params, tokens, t0, max_seq, cache, logits, ws, ws_bytes, stream):
+    _check("nc_prefill", _lib.nc_prefill(C.byref(cfg), params, tokens, t0, max_seq, cache, logits,
+                                         ws, ws_bytes, stream))
+
+
+def nc_decode_step(cfg, params, tokens, pos, max_seq, cache, logits, ws, ws_bytes, stream):
+    _check("nc_decode_step", _lib.nc_decode_step(C.byref(cfg), params, tokens, pos, max_seq,
+                                                 cache, logits, ws, ws_bytes, stream))
 
 
 def nc_status_string(code: int) -> str:
@@ -440,3 +470,34 @@ class Optimizer:
         arr = ((n * 4 + 255) // 256) * 256 // 4
         f = self.state.view(torch.float32)
         return self.m.unpack(f[arr:arr + n]), self.m.unpack(f[2 * arr:2 * arr + n])
+
+
+class Generator:
+    """KV cache and workspace for prefill + decode of a Model (torch buffers)."""
+
+    def __init__(self, model: Model, max_seq: int, max_prefill: int = 0):
+        torch = model.torch
+        self.m = model
+        self.max_seq = max_seq
+        self.cache = torch.empty(nc_kv_cache_size(model.c, max_seq), dtype=torch.uint8,
+                                 device=model.device)
+        self.ws = torch.empty(max(nc_infer_workspace_size(model.c, max_seq, max_prefill), 256),
+                              dtype=torch.uint8, device=model.device)
+        self.logits = torch.empty((model.c.batch, model.c.vocab), dtype=torch.float32,
+                                  device=model.device)
+
+    def prefill(self, params, tokens):
+        """tokens [B, t0] (t0 a multiple of 64); returns the logits at t0-1."""
+        tok = self.m._tok(tokens)
+        nc_prefill(self.m.c, params.data_ptr(), tok.data_ptr(), tok.shape[1], self.max_seq,
+                   self.cache.data_ptr(), self.logits.data_ptr(), self.ws.data_ptr(),
+                   self.ws.numel(), self.m.stream())
+        return self.logits
+
+    def decode(self, params, tokens, pos: int):
+        """tokens [B] at position pos; returns the logits at pos."""
+        tok = self.m._tok(tokens)
+        nc_decode_step(self.m.c, params.data_ptr(), tok.data_ptr(), pos, self.max_seq,
+                       self.cache.data_ptr(), self.logits.data_ptr(), self.ws.data_ptr(),
+                       self.ws.numel(), self.m.stream())
+        return self.logits

@@ -151,6 +151,36 @@ template <typename T>
 hipError_t transpose(const T* in, int rows, int cols, int64_t ld_in, T* out,
                      int64_t ld_out, hipStream_t s);
 
+// ----------------------------------------------------------------- generation
+// y[b][n] = epi(sum_k x[b][k] W[n][k]) for B <= 32 rows (W [N][K], K a
+// multiple of 64): mode EPI_ROWSCALE, EPI_ROWSCALE_RELU2, EPI_RESID (aux
+// [B][N] with ld ldy) into bf16 y, or EPI_STORE_F32 for fp32 y = rs[b] * acc.
+hipError_t gemv(int mode, const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
+                const float* rs, const bf16_t* aux, void* y, int64_t ldy, hipStream_t s);
+// rotary at position pos + QK-norm of B tokens' qkv rows ([B][(H+2) hd], row
+// stride ldq): query heads into q_out fp32 [B][H][hd], the key head and the
+// value head into cache row pos of kc, vc ([B][max_seq][hd])
+template <typename T>
+hipError_t decode_rope(const T* qkv, int64_t ldq, int B, int H, int hd, int pos,
+                       const float* cos_t, const float* sin_t, float eps, float* q_out, T* kc,
+                       T* vc, int max_seq, hipStream_t s);
+// number of key chunks decode_attn splits npos keys into
+int decode_chunks(int npos);
+// o [B][H*hd] = attention of q over cache rows 0..npos-1 (H <= 16, hd <= 128);
+// part_o [B][chunks][H][hd], part_ml [B][chunks][H][2] scratch
+template <typename T>
+hipError_t decode_attn(const float* q, const T* kc, const T* vc, int max_seq, int npos, int B,
+                       int H, int hd, float* part_o, float* part_ml, T* o, hipStream_t s);
+// key and value rows of B*t0 prefill tokens (qkv rows, stride ldq) into the cache
+template <typename T>
+hipError_t cache_fill(const T* qkv, int64_t ldq, int B, int t0, int H, int hd, T* kc, T* vc,
+                      int max_seq, hipStream_t s);
+// out [B][D] = rows b*t0 + t0-1 of x [B*t0][D]
+template <typename T>
+hipError_t gather_last(const T* x, int D, int t0, int B, T* out, hipStream_t s);
+// z = cap * tanh(z / cap) over n fp32 values
+hipError_t softcap_rows(float* z, int64_t n, float cap, hipStream_t s);
+
 // ----------------------------------------------------------------- embedding grad
 // Deterministic scatter-add of de rows into dwte (fully overwritten):
 // dwte[v] = sum over t with tok[t] == v of de[t], summed in position order.

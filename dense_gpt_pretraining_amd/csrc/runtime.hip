@@ -14,6 +14,7 @@
 // r, and in the backward pass the same row scale is folded into the gradient
 // dy' = r dy.  Then dW = dy'^T x and, with dn' = dy' W, the input gradient is
 // dx = dn' - r^2 x mean(dn' * x).
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -22,6 +23,7 @@
 #include <vector>
 
 #include "../../include/nc.h"
+#include "../../include/nc_infer.h"
 #include "kernels.h"
 
 namespace {
@@ -120,7 +122,7 @@ hipError_t gemm_w(int M, int N, int K, const T* A, int64_t lda, const T* W, int6
     return nc::gemm<T>(M, N, K, A, lda, true, W, ldw, false, C, ldc, e, nullptr, 0, s);
 }
 
-Plan make_plan(const nc_config& c, bool bwd, bool recompute = false) {
+Plan make_plan(const nc_config& c, bool bwd, bool recompute = false, bool infer = false) {
     Plan p;
     p.recompute = bwd && recompute;
     const int64_t N = (int64_t)c.batch * c.seq_len;
@@ -146,8 +148,9 @@ Plan make_plan(const nc_config& c, bool bwd, bool recompute = false) {
     p.r2 = take((size_t)p.slots * align256(N * 4));
     p.g = take((size_t)p.slots * align256(N * F * es));
     p.rf = take((size_t)N * 4);
-    p.z = take((size_t)N * Vp * es);
-    p.tok_loss = take((size_t)N * 4);
+    // prefill reads the logits of one position per sequence only
+    p.z = take(infer ? 0 : (size_t)N * Vp * es);
+    p.tok_loss = take(infer ? 0 : (size_t)N * 4);
     p.loss_tmp = take(16);
     if (bwd) {
         p.dres = take((size_t)N * D * 4);
@@ -361,6 +364,29 @@ struct Step {
     // them all, a single one without backward or with recompute
     int slot_of(int l) const { return p.slots > 1 ? l : 0; }
 
+    // Prefill: the forward of the blocks over B sequences of seq_len
+    // positions, writing every layer's key and value rows into the cache;
+    // returns the last block's output (nullptr on a failed launch).
+    T* prefill_blocks(const int32_t* tok, T* cache, int max_seq) {
+        const float eps = c.rms_eps;
+        const double rowb = (double)N * D * es();
+        auto fail = [](hipError_t e) { g_last_hip_error = (int)e; };
+        hipError_t e = nc::rope_tables(c.seq_len, (int)hd, c.rope_base, at<float>(p.cos_t),
+                                       at<float>(p.sin_t), s);
+        if (e == hipSuccess)
+            e = nc::embed_fwd<T>(W(i_wte()), tok, (int)N, (int)D, eps, X(0), at<float>(p.r0), s);
+        if (e != hipSuccess) { fail(e); return nullptr; }
+        (void)rowb;
+        const int64_t per = (int64_t)c.batch * max_seq * hd;
+        for (int l = 0; l < c.n_layer; ++l) {
+            if (layer_fwd(l, 0, X(l & 1), X((l + 1) & 1), true) != NC_OK) return nullptr;
+            e = nc::cache_fill<T>(QKV(0), Wq, c.batch, c.seq_len, (int)H, (int)hd,
+                                  cache + 2 * l * per, cache + (2 * l + 1) * per, max_seq, s);
+            if (e != hipSuccess) { fail(e); return nullptr; }
+        }
+        return X(c.n_layer & 1);
+    }
+
     int forward(const int32_t* tok, const int32_t* tgt, float* loss, float* tok_loss, bool bwd) {
         const float eps = c.rms_eps;
         float* cos_t = at<float>(p.cos_t);
@@ -540,6 +566,155 @@ int check_common(const nc_config* cfg, const void* params, const int32_t* tok,
     if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(tok, 16) || !aligned(tgt, 16) ||
         !aligned(loss, 4) || (tok_loss && !aligned(tok_loss, 16)))
         return NC_ERR_ALIGN;
+    return NC_OK;
+}
+
+// ------------------------------------------------------------------ generation
+// Decode workspace for B tokens and a cache of max_seq positions.
+struct DecPlan {
+    size_t x0, x1, xm, r, qkv, q, o, g, part_o, part_ml, cos_t, sin_t, bytes = 0;
+};
+
+DecPlan make_dec_plan(const nc_config& c, int max_seq) {
+    DecPlan d;
+    const int64_t B = c.batch, D = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_mlp;
+    const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+    const int64_t nch = nc::decode_chunks(max_seq);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t r = off; off += align256(bytes); return r; };
+    d.x0 = take(B * D * es);
+    d.x1 = take(B * D * es);
+    d.xm = take(B * D * es);
+    d.r = take(B * 4);
+    d.qkv = take(B * (H + 2) * hd * es);
+    d.q = take(B * H * hd * 4);
+    d.o = take(B * H * hd * es);
+    d.g = take(B * F * es);
+    d.part_o = take(B * nch * H * hd * 4);
+    d.part_ml = take(B * nch * H * 2 * 4);
+    d.cos_t = take((size_t)max_seq * (hd / 2) * 4);
+    d.sin_t = take((size_t)max_seq * (hd / 2) * 4);
+    d.bytes = off;
+    return d;
+}
+
+// config the training kernels see for a prefill of t0 positions
+nc_config prefill_cfg(const nc_config& c, int t0) {
+    nc_config p = c;
+    p.seq_len = t0;
+    return p;
+}
+
+size_t prefill_bytes(const nc_config& c, int t0) {
+    const nc_config pc = prefill_cfg(c, t0);
+    const size_t es = c.dtype == NC_BF16 ? 2 : 4;
+    return make_plan(pc, false, false, true).bytes + align256((size_t)c.batch * c.d_model * es) +
+           align256((size_t)c.batch * 4);
+}
+
+int check_infer(const nc_config* cfg, int max_seq) {
+    if (!cfg) return NC_ERR_NULL;
+    nc_config probe = *cfg;
+    probe.seq_len = 64;   // the step's own length check does not apply here
+    int rc = validate(&probe);
+    if (rc != NC_OK) return rc;
+    if (max_seq < 1) return NC_ERR_CONFIG;
+    if (cfg->n_head > 16) return NC_ERR_UNSUPPORTED;   // decode attention keeps 16 heads
+    return NC_OK;
+}
+
+// decode-step product y = epi(x W^T) of B rows: the weight-streaming matrix-
+// core kernel for bf16, the SIMT product for fp32 (logits: EPI_STORE_F32)
+template <typename T>
+hipError_t dec_gemm(int mode, const T* x, int64_t ldx, int B, const T* W, int N, int K,
+                    const float* rs, const T* aux, void* y, int64_t ldy, hipStream_t s) {
+    if constexpr (std::is_same<T, nc::bf16_t>::value) {
+        return nc::gemv(mode, x, ldx, B, W, N, K, rs, aux, y, ldy, s);
+    } else {
+        nc::Epilogue e;
+        e.mode = mode == nc::EPI_STORE_F32 ? nc::EPI_ROWSCALE : mode;
+        e.rowscale = rs;
+        e.aux = aux;
+        return nc::gemm<float>(B, N, K, x, ldx, true, W, K, true, y, ldy, e, nullptr, 0, s);
+    }
+}
+
+template <typename T>
+int decode_step(const nc_config& c, const T* params, const int32_t* tok, int pos, int max_seq,
+                T* cache, float* logits, char* ws, hipStream_t s) {
+    const DecPlan d = make_dec_plan(c, max_seq);
+    std::vector<TensorDesc> lay = layout(c, nullptr);
+    const int B = c.batch, D = c.d_model, H = c.n_head, hd = c.head_dim, F = c.d_mlp,
+              V = c.vocab, L = c.n_layer;
+    const int Wq = (H + 2) * hd;
+    const float eps = c.rms_eps;
+    auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+    float* r = reinterpret_cast<float*>(ws + d.r);
+    float* q = reinterpret_cast<float*>(ws + d.q);
+    float* cos_t = reinterpret_cast<float*>(ws + d.cos_t);
+    float* sin_t = reinterpret_cast<float*>(ws + d.sin_t);
+    const T* Wt = params;
+    auto Wl = [&](int l, int k) { return Wt + lay[1 + 6 * l + k].offset; };
+    const int64_t per = (int64_t)B * max_seq * hd;
+    NC_TRY(nc::rope_tables(pos + 1, hd, c.rope_base, cos_t, sin_t, s));
+    T* x = P(d.x0);
+    T* xn = P(d.x1);
+    T* xm = P(d.xm);
+    NC_TRY(nc::embed_fwd<T>(Wt + lay[0].offset, tok, B, D, eps, x, r, s));
+    for (int l = 0; l < L; ++l) {
+        T* kc = cache + 2 * l * per;
+        T* vc = cache + (2 * l + 1) * per;
+        NC_TRY(nc::rms_stats<T>(x, B, D, eps, r, s));
+        NC_TRY(dec_gemm<T>(nc::EPI_ROWSCALE, x, D, B, Wl(l, 0), Wq, D, r, nullptr, P(d.qkv), Wq,
+                           s));
+        NC_TRY(nc::decode_rope<T>(P(d.qkv), Wq, B, H, hd, pos, cos_t, sin_t, eps, q, kc, vc,
+                                  max_seq, s));
+        NC_TRY(nc::decode_attn<T>(q, kc, vc, max_seq, pos + 1, B, H, hd,
+                                  reinterpret_cast<float*>(ws + d.part_o),
+                                  reinterpret_cast<float*>(ws + d.part_ml), P(d.o), s));
+        NC_TRY(dec_gemm<T>(nc::EPI_RESID, P(d.o), H * hd, B, Wl(l, 3), D, H * hd, nullptr, x, xm,
+                           D, s));
+        NC_TRY(nc::rms_stats<T>(xm, B, D, eps, r, s));
+        NC_TRY(dec_gemm<T>(nc::EPI_ROWSCALE_RELU2, xm, D, B, Wl(l, 4), F, D, r, nullptr, P(d.g),
+                           F, s));
+        NC_TRY(dec_gemm<T>(nc::EPI_RESID, P(d.g), F, B, Wl(l, 5), D, F, nullptr, xm, xn, D, s));
+        std::swap(x, xn);
+    }
+    NC_TRY(nc::rms_stats<T>(x, B, D, eps, r, s));
+    NC_TRY(dec_gemm<T>(nc::EPI_STORE_F32, x, D, B, Wt + lay[1 + 6 * L].offset, V, D, r, nullptr,
+                       logits, V, s));
+    NC_TRY(nc::softcap_rows(logits, (int64_t)B * V, c.softcap, s));
+    return NC_OK;
+}
+
+template <typename T>
+int prefill(const nc_config& c, const T* params, const int32_t* tok, int t0, int max_seq,
+            T* cache, float* logits, char* ws, hipStream_t s) {
+    const nc_config pc = prefill_cfg(c, t0);
+    const Plan p = make_plan(pc, false, false, true);
+    Step<T> st(pc, p, ws, s, params, nullptr);
+    T* hL = st.prefill_blocks(tok, cache, max_seq);
+    if (!hL) return NC_ERR_HIP;
+    const size_t es = sizeof(T);
+    T* last = reinterpret_cast<T*>(ws + p.bytes);
+    float* rf = reinterpret_cast<float*>(ws + p.bytes + align256((size_t)c.batch * c.d_model * es));
+    const int B = c.batch, D = c.d_model;
+    NC_TRY(nc::gather_last<T>(hL, D, t0, B, last, s));
+    NC_TRY(nc::rms_stats<T>(last, B, D, c.rms_eps, rf, s));
+    std::vector<TensorDesc> lay = layout(c, nullptr);
+    if (B > 32 && std::is_same<T, nc::bf16_t>::value) {
+        // the weight-streaming product takes 32 rows at a time
+        for (int b0 = 0; b0 < B; b0 += 32) {
+            const int nb = std::min(32, B - b0);
+            NC_TRY(dec_gemm<T>(nc::EPI_STORE_F32, last + (int64_t)b0 * D, D, nb,
+                               params + lay.back().offset, c.vocab, D, rf + b0, nullptr,
+                               logits + (int64_t)b0 * c.vocab, c.vocab, s));
+        }
+    } else {
+        NC_TRY(dec_gemm<T>(nc::EPI_STORE_F32, last, D, B, params + lay.back().offset, c.vocab, D,
+                           rf, nullptr, logits, c.vocab, s));
+    }
+    NC_TRY(nc::softcap_rows(logits, (int64_t)B * c.vocab, c.softcap, s));
     return NC_OK;
 }
 
@@ -736,6 +911,70 @@ int nc_validate_tokens(const nc_config* cfg, const int32_t* tokens, const int32_
     NC_TRY(nc::count_bad_ids(tokens, targets, (int64_t)cfg->batch * cfg->seq_len, cfg->vocab,
                              n_bad, s));
     return NC_OK;
+}
+
+int nc_kv_cache_size(const nc_config* cfg, int32_t max_seq, size_t* bytes) {
+    int rc = check_infer(cfg, max_seq);
+    if (rc != NC_OK) return rc;
+    if (!bytes) return NC_ERR_NULL;
+    const size_t es = cfg->dtype == NC_BF16 ? 2 : 4;
+    *bytes = align256((size_t)2 * cfg->n_layer * cfg->batch * max_seq * cfg->head_dim * es);
+    return NC_OK;
+}
+
+int nc_infer_workspace_size(const nc_config* cfg, int32_t max_seq, int32_t t0, size_t* bytes) {
+    int rc = check_infer(cfg, max_seq);
+    if (rc != NC_OK) return rc;
+    if (!bytes) return NC_ERR_NULL;
+    if (t0 < 0 || t0 > max_seq || t0 % 64) return NC_ERR_CONFIG;
+    size_t b = make_dec_plan(*cfg, max_seq).bytes;
+    if (t0 > 0) b = std::max(b, prefill_bytes(*cfg, t0));
+    *bytes = b;
+    return NC_OK;
+}
+
+int nc_prefill(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t t0,
+               int32_t max_seq, void* cache, float* logits, void* ws, size_t ws_bytes,
+               void* stream) {
+    int rc = check_infer(cfg, max_seq);
+    if (rc != NC_OK) return rc;
+    if (t0 < 64 || t0 > max_seq || t0 % 64) return NC_ERR_CONFIG;
+    const nc_config pc = prefill_cfg(*cfg, t0);
+    rc = validate(&pc);
+    if (rc != NC_OK) return rc;
+    if (!params || !tokens || !cache || !logits || !ws) return NC_ERR_NULL;
+    if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(cache, 256) ||
+        !aligned(tokens, 16) || !aligned(logits, 16))
+        return NC_ERR_ALIGN;
+    if (ws_bytes < prefill_bytes(*cfg, t0)) return NC_ERR_WORKSPACE;
+    hipStream_t s = nc::enqueue_stream(stream);
+    char* w = static_cast<char*>(ws);
+    if (cfg->dtype == NC_BF16)
+        return prefill<nc::bf16_t>(*cfg, static_cast<const nc::bf16_t*>(params), tokens, t0,
+                                   max_seq, static_cast<nc::bf16_t*>(cache), logits, w, s);
+    return prefill<float>(*cfg, static_cast<const float*>(params), tokens, t0, max_seq,
+                          static_cast<float*>(cache), logits, w, s);
+}
+
+int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t pos,
+                   int32_t max_seq, void* cache, float* logits, void* ws, size_t ws_bytes,
+                   void* stream) {
+    int rc = check_infer(cfg, max_seq);
+    if (rc != NC_OK) return rc;
+    if (pos < 0 || pos >= max_seq) return NC_ERR_CONFIG;
+    if (cfg->batch > 32) return NC_ERR_UNSUPPORTED;
+    if (!params || !tokens || !cache || !logits || !ws) return NC_ERR_NULL;
+    if (!aligned(params, 256) || !aligned(ws, 256) || !aligned(cache, 256) ||
+        !aligned(tokens, 4) || !aligned(logits, 16))
+        return NC_ERR_ALIGN;
+    if (ws_bytes < make_dec_plan(*cfg, max_seq).bytes) return NC_ERR_WORKSPACE;
+    hipStream_t s = nc::enqueue_stream(stream);
+    char* w = static_cast<char*>(ws);
+    if (cfg->dtype == NC_BF16)
+        return decode_step<nc::bf16_t>(*cfg, static_cast<const nc::bf16_t*>(params), tokens, pos,
+                                       max_seq, static_cast<nc::bf16_t*>(cache), logits, w, s);
+    return decode_step<float>(*cfg, static_cast<const float*>(params), tokens, pos, max_seq,
+                              static_cast<float*>(cache), logits, w, s);
 }
 
 const char* nc_status_string(int status) {

@@ -268,3 +268,36 @@ def test_binding_and_torch_share_one_hip_runtime():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
+def test_generation_validation_before_device_work():
+    b = _b()
+    cfg = get_config("d20", batch=4)
+    c = b.make_config(cfg)
+    cache = b.nc_kv_cache_size(c, 320)
+    assert cache == 2 * 20 * 4 * 320 * 128 * 2
+    ws_dec = b.nc_infer_workspace_size(c, 320, 0)
+    ws_pre = b.nc_infer_workspace_size(c, 320, 256)
+    assert ws_pre >= ws_dec > 0
+    for t0, code in ((100, -2), (0, -2), (384, -2)):
+        with pytest.raises(b.NcError) as ei:
+            b.nc_prefill(c, 0x1000, 0x2000, t0, 320, 0x3000, 0x4000, 0x5000, ws_pre, None)
+        assert ei.value.code == code, t0
+    with pytest.raises(b.NcError) as ei:
+        b.nc_prefill(c, 0x1000, 0x2000, 256, 320, 0x3000, 0x4000, 0x5000, ws_pre - 1, None)
+    assert ei.value.code == -4
+    for pos, code in ((-1, -2), (320, -2)):
+        with pytest.raises(b.NcError) as ei:
+            b.nc_decode_step(c, 0x1000, 0x2000, pos, 320, 0x3000, 0x4000, 0x5000, ws_dec, None)
+        assert ei.value.code == code, pos
+    with pytest.raises(b.NcError) as ei:
+        b.nc_decode_step(c, 0x1000, 0x2000, 5, 320, 0x3000 + 64, 0x4000, 0x5000, ws_dec, None)
+    assert ei.value.code == -5
+    big = b.make_config({**cfg, "batch": 33})
+    with pytest.raises(b.NcError) as ei:
+        b.nc_decode_step(big, 0x1000, 0x2000, 5, 320, 0x3000, 0x4000, 0x5000, 1 << 40, None)
+    assert ei.value.code == -7
+    heads = b.make_config({**cfg, "n_head": 17})
+    with pytest.raises(b.NcError) as ei:
+        b.nc_kv_cache_size(heads, 320)
+    assert ei.value.code == -7
