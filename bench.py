@@ -159,6 +159,44 @@ def optimizer_timing(model, params, grads, cfg, steps):
                     "AdamW on wte and wlm, global-norm clipping; not part of the fwd+bwd metric"}
 
 
+def generation_timing(model, params, cfg, tokens):
+    """Prefill of the batch's first T-64 positions, then 64 decode steps (one
+    token per sequence each) up to position T-1; HBM bytes of a decode step:
+    every matrix weight read once, the embedding rows and the cache rows the
+    step reads (keys and values of every earlier position, all layers)."""
+    import torch
+
+    from dense_gpt_pretraining_amd import Generator
+    B, T = tokens.shape
+    t0 = T - 64
+    gen = Generator(model, max_seq=T, max_prefill=t0)
+    tok = torch.from_numpy(tokens).cuda()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    gen.prefill(params, tok[:, :t0])          # warm-up of the prefill path
+    torch.cuda.synchronize()
+    ev[0].record()
+    gen.prefill(params, tok[:, :t0])
+    ev[1].record()
+    for pos in range(t0, T):
+        gen.decode(params, tok[:, pos], pos)
+    ev[2].record()
+    torch.cuda.synchronize()
+    pre_ms = ev[0].elapsed_time(ev[1])
+    dec_ms = ev[1].elapsed_time(ev[2]) / (T - t0)
+    D, H, hd, F, V, L = (cfg[k] for k in ("d_model", "n_head", "head_dim", "d_mlp", "vocab",
+                                          "n_layer"))
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    w_bytes = (L * ((H + 2) * hd * D + D * H * hd + 2 * F * D) + V * D) * es + B * D * es
+    mean_pos = (t0 + T - 1) / 2.0 + 1
+    kv_bytes = 2 * L * B * mean_pos * hd * es
+    return {"prefill_ms": round(pre_ms, 3), "prefill_tokens_per_s": round(B * t0 / pre_ms * 1e3, 1),
+            "decode_ms_per_step": round(dec_ms, 4),
+            "decode_tokens_per_s": round(B / dec_ms * 1e3, 1),
+            "decode_hbm_gb_per_step": round((w_bytes + kv_bytes) / 1e9, 4),
+            "decode_hbm_gbs": round((w_bytes + kv_bytes) / (dec_ms / 1e3) / 1e9, 1),
+            "shape": f"batch {B}, prefill {t0} positions, decode positions {t0}..{T - 1}"}
+
+
 def cpu_baseline(cfg):
     """The oracle's fwd+bwd on one sequence of the workload, on host cores."""
     import numpy as np
@@ -189,6 +227,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="d20")
     ap.add_argument("--profile-reps", type=int, default=3)
+    ap.add_argument("--generation", type=int, default=1,
+                    help="also time prefill and KV-cache decode steps (1) or not (0)")
     ap.add_argument("--optimizer", type=int, default=1,
                     help="also time one Muon + AdamW optimizer step (1) or not (0)")
     args = ap.parse_args()
@@ -261,6 +301,7 @@ def main():
         e["gbs"] = round(v["bytes"] / (v["ms"] / 1e3) / 1e9, 1)
         kernels.append(e)
 
+    gen = generation_timing(model, params, cfg, tokens) if args.generation else None
     optim = optimizer_timing(model, params, grads, cfg, 5) if args.optimizer else None
 
     cpu = cpu_baseline(cfg)
@@ -289,6 +330,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "optimizer_step": optim,
+        "generation": gen,
         "kernels": kernels,
     }
     print(json.dumps(out))
