@@ -108,6 +108,8 @@ _sigs = {
                              C.c_size_t, _P]),
     "nc_decode_step": (C.c_int, [C.POINTER(nc_config), _P, _P, C.c_int32, C.c_int32, _P, _P, _P,
                                  C.c_size_t, _P]),
+    "nc_decode_step_noalloc": (C.c_int, [C.POINTER(nc_config), _P, _P, C.c_int32, C.c_int32,
+                                         _P, _P, _P]),
     "nc_op_matmul": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
                                C.c_int32, _P, C.c_int64, C.c_int32, _P, C.c_int64, _P,
                                C.c_size_t, _P]),
@@ -284,6 +286,11 @@ def nc_prefill(cfg, params, tokens, t0, max_seq, cache, logits, ws, ws_bytes, st
 def nc_decode_step(cfg, params, tokens, pos, max_seq, cache, logits, ws, ws_bytes, stream):
     _check("nc_decode_step", _lib.nc_decode_step(C.byref(cfg), params, tokens, pos, max_seq,
                                                  cache, logits, ws, ws_bytes, stream))
+
+
+def nc_decode_step_noalloc(cfg, params, tokens, pos, max_seq, cache, logits, stream):
+    _check("nc_decode_step_noalloc", _lib.nc_decode_step_noalloc(
+        C.byref(cfg), params, tokens, pos, max_seq, cache, logits, stream))
 
 
 def nc_status_string(code: int) -> str:

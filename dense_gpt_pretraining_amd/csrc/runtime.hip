@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -570,6 +571,39 @@ int check_common(const nc_config* cfg, const void* params, const int32_t* tok,
 }
 
 // ------------------------------------------------------------------ generation
+// Decode workspace of nc_decode_step_noalloc, for callers that cannot
+// allocate device memory: one array per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): each device's address is looked up once,
+// with that device current, and kept.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return NC_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return NC_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_hip_error = (int)e;
+            return NC_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return NC_OK;
+}
+
 // Decode workspace for B tokens and a cache of max_seq positions.
 struct DecPlan {
     size_t x0, x1, xm, r, qkv, q, o, g, part_o, part_ml, cos_t, sin_t, bytes = 0;
@@ -968,6 +1002,30 @@ int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* toke
         !aligned(tokens, 4) || !aligned(logits, 16))
         return NC_ERR_ALIGN;
     if (ws_bytes < make_dec_plan(*cfg, max_seq).bytes) return NC_ERR_WORKSPACE;
+    hipStream_t s = nc::enqueue_stream(stream);
+    char* w = static_cast<char*>(ws);
+    if (cfg->dtype == NC_BF16)
+        return decode_step<nc::bf16_t>(*cfg, static_cast<const nc::bf16_t*>(params), tokens, pos,
+                                       max_seq, static_cast<nc::bf16_t*>(cache), logits, w, s);
+    return decode_step<float>(*cfg, static_cast<const float*>(params), tokens, pos, max_seq,
+                              static_cast<float*>(cache), logits, w, s);
+}
+
+int nc_decode_step_noalloc(const nc_config* cfg, const void* params, const int32_t* tokens,
+                           int32_t pos, int32_t max_seq, void* cache, float* logits,
+                           void* stream) {
+    int rc = check_infer(cfg, max_seq);
+    if (rc != NC_OK) return rc;
+    if (pos < 0 || pos >= max_seq) return NC_ERR_CONFIG;
+    if (cfg->batch > 32) return NC_ERR_UNSUPPORTED;
+    if (!params || !tokens || !cache || !logits) return NC_ERR_NULL;
+    if (!aligned(params, 256) || !aligned(cache, 256) || !aligned(tokens, 4) ||
+        !aligned(logits, 16))
+        return NC_ERR_ALIGN;
+    if (make_dec_plan(*cfg, max_seq).bytes > kDecodeScratchBytes) return NC_ERR_WORKSPACE;
+    void* ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc != NC_OK) return rc;
     hipStream_t s = nc::enqueue_stream(stream);
     char* w = static_cast<char*>(ws);
     if (cfg->dtype == NC_BF16)

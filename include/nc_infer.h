@@ -65,6 +65,22 @@ int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* toke
                    int32_t pos, int32_t max_seq, void* cache, float* logits, void* ws,
                    size_t ws_bytes, void* stream);
 
+/*
+ * nc_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step with its workspace in a 32 MiB array the library holds on
+ * every GPU it runs on until the process ends, instead of a `ws` argument.
+ * Its kernels are nc_decode_step's and the results are bitwise the same.
+ * NC_ERR_WORKSPACE when the step needs more than 32 MiB (nc_infer_workspace_
+ * size(cfg, max_seq, 0) > 32 MiB; the depth-20 shapes need about 11 MiB at
+ * batch 32 and max_seq 8192).  The array holds the last call's values (the
+ * step writes every byte it reads); calls that overlap on one GPU, on any
+ * streams, race on it.
+ */
+int nc_decode_step_noalloc(const nc_config* cfg, const void* params, const int32_t* tokens,
+                           int32_t pos, int32_t max_seq, void* cache, float* logits,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif
