@@ -356,14 +356,15 @@ __device__ __forceinline__ void epi_vec4_pre(const EpiDev& e, void* C, int64_t i
 // with i + hd/2, which sits hd/8 lanes away -- and RMS-normalised over its
 // group; the value head is stored as u.
 __device__ __forceinline__ void qkv_rope_store(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
-                                               int N, int64_t m, int64_t n, float4 v) {
+                                               int N, int64_t m, int64_t n, float4 v,
+                                               float rs_m) {
     // 32-bit index arithmetic (rows < 2^24, columns < 2^16); head_dim is a
     // power of two
     const int hd = e.head_dim, half = hd >> 1, H = e.n_head;
     const int hd_shift = __builtin_ctz((unsigned)hd);
     const int mi = (int)m, ni = (int)n;
     const bool valid = mi < M && ni < N;
-    const float rs = valid ? e.rowscale[mi] : 0.f;
+    const float rs = valid ? rs_m : 0.f;
     float x[4] = {v.x * rs, v.y * rs, v.z * rs, v.w * rs};
     const int head = ni >> hd_shift;             // uniform over the lane group
     const int d = ni & (hd - 1);                 // first of this lane's 4 elements
@@ -413,7 +414,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 // rows x 128 columns (16-byte chunk c of row r at chunk position c ^ r).
 __device__ __forceinline__ void qkv_rope_pass128(const EpiDev& e, bf16_t* C, int64_t ldc, int M,
                                                  int N, const float* stage, int mrow0,
-                                                 int ncol0, int lane) {
+                                                 int ncol0, int lane, const float* rsl) {
     if (ncol0 >= N) return;
     const int H = e.n_head;
     const int head = ncol0 >> 7;
@@ -427,7 +428,7 @@ __device__ __forceinline__ void qkv_rope_pass128(const EpiDev& e, bf16_t* C, int
         const float4 b =
             *reinterpret_cast<const float4*>(stage + row * 128 + (((16 + l16) ^ row) << 2));
         const bool valid = mi < M;
-        const float rs = valid ? e.rowscale[mi] : 0.f;
+        const float rs = valid ? rsl[row] : 0.f;
         float x1[4] = {a.x * rs, a.y * rs, a.z * rs, a.w * rs};
         float x2[4] = {b.x * rs, b.y * rs, b.z * rs, b.w * rs};
         if (rot) {
@@ -485,6 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     __shared__ __align__(16) bf16_t ldsA1[kTileElems];
     __shared__ __align__(16) bf16_t ldsB0[kTileElems];
     __shared__ __align__(16) bf16_t ldsB1[kTileElems];
+    // the tile's row scales, copied into LDS with the first k tile: the
+    // epilogue reads them there instead of waiting on global loads
+    __shared__ __align__(16) float lds_rs[kTM];
 
     const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
     const int total = tiles_m * tiles_n;
@@ -580,10 +584,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
                                                          m * ldc + n);
         }
     };
-    if (nk > 0) {
-        issue(0, ldsA0, ldsB0);
-        wait_vmem();
+    constexpr bool kRsMode = MODE == EPI_ROWSCALE || MODE == EPI_ROWSCALE_RELU2 ||
+                             MODE == EPI_RELU2_BWD || MODE == EPI_QKV_ROPE;
+    if (kRsMode && wave == 0) {
+        const buf_rsrc_t r = make_rsrc(e.rowscale + m0);
+#pragma unroll
+        for (int i = 0; i < kTM / 64; ++i)
+            lds_copy<4>(r, m0 + 64 * i + lane < M ? (64 * i + lane) * 4 : kOutOfRange,
+                        lds_rs + 64 * i);
     }
+    if (nk > 0) issue(0, ldsA0, ldsB0);
+    wait_vmem();
     __syncthreads();
     {
         // fragments of k step ks+1 are read while the 8 matrix instructions
@@ -690,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int64_t m = m0 + wm * 64 + 32 * j + 2 * t + hi;
-            rsv[t] = (kRs && m < M) ? e.rowscale[m] : 0.f;
+            rsv[t] = (kRs && m < M) ? lds_rs[m - m0] : 0.f;
             if (!kAux) auxv[t] = make_uint2(0, 0);
         }
 #pragma unroll
@@ -706,7 +717,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
         const int64_t n = n0 + wn * 128 + 4 * li;
         if (MODE == EPI_QKV_ROPE && e.head_dim == 128) {
             qkv_rope_pass128(e, static_cast<bf16_t*>(C), ldc, M, N, stage, m0 + wm * 64 + 32 * j,
-                             n0 + wn * 128, lane);
+                             n0 + wn * 128, lane, lds_rs + wm * 64 + 32 * j);
         } else
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -715,7 +726,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
             const int64_t m = m0 + wm * 64 + 32 * j + row;
             if (MODE == EPI_QKV_ROPE) {
                 // every lane of the half-wave joins the head's shuffles
-                qkv_rope_store(e, static_cast<bf16_t*>(C), ldc, M, N, m, n, v);
+                qkv_rope_store(e, static_cast<bf16_t*>(C), ldc, M, N, m, n, v,
+                               m < M ? lds_rs[m - m0] : 0.f);
                 continue;
             }
             if (m >= M) continue;

@@ -18,11 +18,15 @@
 //     are summed in LDS in a fixed order and the epilogue (row scale,
 //     relu^2, residual) applied there.  The fp32 configuration uses the
 //     SIMT product of the GEMM family.
+//     When N / 32 workgroups cannot keep the compute units streaming, the k
+//     range is also cut into slices (raw sums to scratch, then a kernel that
+//     adds them in slice order and applies the epilogue).
 //   * Attention of the H query heads of a token over its cache is split
-//     over chunks of 256 keys (flash-decoding): each workgroup scores one
-//     chunk for every head (one key per thread, the key row read once for
-//     all H heads), keeps the chunk's max and sum per head and its weighted
-//     value sum; a second kernel merges the chunks.
+//     over chunks of 128 keys (flash-decoding): each workgroup scores one
+//     chunk for every head (two threads per key, the key row read once for
+//     all H heads), stages the chunk's value rows in LDS, keeps the chunk's
+//     max and sum per head and its weighted value sum; a second kernel
+//     merges the chunks.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -37,26 +41,31 @@ namespace {
 
 constexpr int kGvThreads = 256;       // 4 waves, each a quarter of the k range
 constexpr int kGvRows = 32;           // rows of W per workgroup
-constexpr int kDecChunk = 256;        // keys per attention workgroup (one per thread)
+constexpr int kDecChunk = 128;        // keys per attention workgroup (two threads per key)
+constexpr int kDecThreads = 2 * kDecChunk;
 constexpr int kMaxHeads = 16;
 
 // y[b][n] = epi(sum_k x[b][k] W[n][k]) for b < B <= 32, n < N; x row stride
 // ldx, W [N][K] (K a multiple of 64), y row stride ldy.
+// With gridDim.y = S > 1 the k range is cut into S slices: slice s writes its
+// raw sums to part[s][b][n] and k_gemv_reduce applies the epilogue.
 template <int MODE>
 __global__ __launch_bounds__(kGvThreads) void k_gemv_mfma(const bf16_t* __restrict__ x,
                                                           int64_t ldx, int B,
                                                           const bf16_t* __restrict__ W, int N,
                                                           int K, const float* __restrict__ rs,
                                                           const bf16_t* __restrict__ aux,
-                                                          void* __restrict__ y, int64_t ldy) {
+                                                          void* __restrict__ y, int64_t ldy,
+                                                          float* __restrict__ split_part) {
     __shared__ float part[4][kGvRows][kGvRows + 1];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n0 = blockIdx.x * kGvRows;
     const int li = lane & 31, g = lane >> 5;
     const int nrow = min(n0 + li, N - 1);               // rows past N repeat the last one
     const bool brow = li < B;
-    const int kq = K / 4;
-    const int kb = w * kq, ke = kb + kq;
+    const int ks = K / (int)gridDim.y;                  // this slice's k range
+    const int kq = ks / 4;
+    const int kb = (int)blockIdx.y * ks + w * kq, ke = kb + kq;
     const bf16_t* wp = W + (int64_t)nrow * K + 8 * g;
     const bf16_t* xp = x + (int64_t)(brow ? li : 0) * ldx + 8 * g;
     f32x16_t acc;
@@ -92,6 +101,10 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_mfma(const bf16_t* __restri
         const int n = n0 + nn;
         if (b >= B || n >= N) continue;
         const float v = ((part[0][nn][b] + part[1][nn][b]) + part[2][nn][b]) + part[3][nn][b];
+        if (gridDim.y > 1) {
+            split_part[((int64_t)blockIdx.y * B + b) * N + n] = v;
+            continue;
+        }
         const int64_t o = (int64_t)b * ldy + n;
         if (MODE == EPI_STORE_F32) {
             static_cast<float*>(y)[o] = rs[b] * v;            // logits z = r f W^T, fp32
@@ -105,6 +118,32 @@ __global__ __launch_bounds__(kGvThreads) void k_gemv_mfma(const bf16_t* __restri
             if (MODE == EPI_RESID) u = bf2f(aux[o]) + v;
             static_cast<bf16_t*>(y)[o] = f2bf(u);
         }
+    }
+}
+
+// the k slices' sums of k_gemv_mfma added in slice order, then its epilogue
+template <int MODE>
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int S, int B,
+                                                     int N, const float* __restrict__ rs,
+                                                     const bf16_t* __restrict__ aux,
+                                                     void* __restrict__ y, int64_t ldy) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)B * N) return;
+    const int b = (int)(i / N), n = (int)(i % N);
+    float v = 0.f;
+    for (int sl = 0; sl < S; ++sl) v += part[(int64_t)sl * B * N + i];
+    const int64_t o = (int64_t)b * ldy + n;
+    if (MODE == EPI_STORE_F32) {
+        static_cast<float*>(y)[o] = rs[b] * v;
+    } else {
+        float u = v;
+        if (MODE == EPI_ROWSCALE) u = rs[b] * v;
+        if (MODE == EPI_ROWSCALE_RELU2) {
+            const float t = fmaxf(rs[b] * v, 0.f);
+            u = t * t;
+        }
+        if (MODE == EPI_RESID) u = bf2f(aux[o]) + v;
+        static_cast<bf16_t*>(y)[o] = f2bf(u);
     }
 }
 
@@ -148,64 +187,75 @@ __global__ __launch_bounds__(64) void k_decode_rope(const T* __restrict__ qkv, i
     }
 }
 
-// Chunk c of token b's keys 0 .. npos-1: per head j the chunk's max m, sum
-// l of exp(s - m) and sum of exp(s - m) v, s = q_j . k / sqrt(hd).
+// Chunk c of token b's keys 0 .. npos-1 (kDecChunk keys): per head j the
+// chunk's max m, sum l of exp(s - m) and sum of exp(s - m) v, with
+// s = q_j . k / sqrt(hd).  Two threads score one key (half of hd each); the
+// chunk's value rows are staged in LDS with 16-byte copies, then thread t
+// forms outputs (j, d) = (t + 256 r) / hd, % hd, reading consecutive d.
 template <typename T>
-__global__ __launch_bounds__(kDecChunk) void k_decode_attn(
+__global__ __launch_bounds__(kDecThreads) void k_decode_attn(
     const float* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, int max_seq,
     int npos, int H, int hd, float scale, int nch, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
     __shared__ float qs[kMaxHeads * 128];
     __shared__ float ps[kMaxHeads * kDecChunk];
-    __shared__ float red[kMaxHeads][kDecChunk / 64];
+    __shared__ __align__(16) T vs[kDecChunk * 128];
+    __shared__ float red[kMaxHeads][kDecThreads / 64];
     const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
-    for (int e = t; e < H * hd; e += kDecChunk) qs[e] = q[(int64_t)b * H * hd + e];
+    const int cnt = min(kDecChunk, npos - c * kDecChunk);
+    for (int e = t; e < H * hd; e += kDecThreads) qs[e] = q[(int64_t)b * H * hd + e];
+    {
+        // value rows c*kDecChunk .. +cnt-1 are contiguous in the cache
+        const uint4* src = reinterpret_cast<const uint4*>(
+            vc + ((int64_t)b * max_seq + (int64_t)c * kDecChunk) * hd);
+        uint4* dst = reinterpret_cast<uint4*>(vs);
+        const int n16 = cnt * hd * (int)sizeof(T) / 16;
+        for (int e = t; e < n16; e += kDecThreads) dst[e] = src[e];
+    }
     __syncthreads();
-    const int key = c * kDecChunk + t;
-    const bool valid = key < npos;
-    const T* krow = kc + ((int64_t)b * max_seq + (valid ? key : 0)) * hd;
+    const int kl = t >> 1, hh = t & 1;
+    const bool valid = kl < cnt;
+    const int half = hd >> 1;
+    const T* krow = kc + ((int64_t)b * max_seq + (int64_t)c * kDecChunk + (valid ? kl : 0)) * hd +
+                    hh * half;
     float s[kMaxHeads];
 #pragma unroll
     for (int j = 0; j < kMaxHeads; ++j) s[j] = 0.f;
     constexpr int kV = Elt<T>::kVec;
-    for (int d0 = 0; d0 < hd; d0 += kV) {
+    for (int d0 = 0; d0 < half; d0 += kV) {
         float kv[kV];
         ld_vec<T>(krow + d0, kv);
 #pragma unroll
         for (int j = 0; j < kMaxHeads; ++j) {
             if (j < H) {
-                const float* qj = qs + j * hd + d0;
+                const float* qj = qs + j * hd + hh * half + d0;
 #pragma unroll
                 for (int e = 0; e < kV; ++e) s[j] = fmaf(qj[e], kv[e], s[j]);
             }
         }
     }
-    float mj[kMaxHeads];
 #pragma unroll
     for (int j = 0; j < kMaxHeads; ++j) {
         if (j < H) {
+            s[j] += __shfl_xor(s[j], 1, 64);
             s[j] = valid ? s[j] * scale : -INFINITY;
             const float m = wave_max(s[j]);
             if (lane == 0) red[j][wv] = m;
         }
     }
     __syncthreads();
+    float mj[kMaxHeads];
 #pragma unroll
-    for (int j = 0; j < kMaxHeads; ++j) {
-        if (j < H) {
-            float m = red[j][0];
-            for (int u = 1; u < kDecChunk / 64; ++u) m = fmaxf(m, red[j][u]);
-            mj[j] = m;
-        }
-    }
+    for (int j = 0; j < kMaxHeads; ++j)
+        mj[j] = j < H ? fmaxf(fmaxf(red[j][0], red[j][1]), fmaxf(red[j][2], red[j][3])) : 0.f;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < kMaxHeads; ++j) {
         if (j < H) {
             const float p = valid ? expf(s[j] - mj[j]) : 0.f;
-            ps[j * kDecChunk + t] = p;
-            const float l = wave_sum(p);
+            if (hh == 0) ps[j * kDecChunk + kl] = p;
+            const float l = wave_sum(hh == 0 ? p : 0.f);
             if (lane == 0) red[j][wv] = l;
         }
     }
@@ -215,45 +265,39 @@ __global__ __launch_bounds__(kDecChunk) void k_decode_attn(
 #pragma unroll
     for (int j = 0; j < kMaxHeads; ++j) {
         if (j < H && t == j) {
-            float l = 0.f;
-            for (int u = 0; u < kDecChunk / 64; ++u) l += red[j][u];
             part_ml[(slot * H + j) * 2] = mj[j];
-            part_ml[(slot * H + j) * 2 + 1] = l;
+            part_ml[(slot * H + j) * 2 + 1] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
         }
     }
-    // weighted value sums: thread t takes dimension t % hd of heads
-    // t / hd, t / hd + 256 / hd, ...
-    const int cnt = min(kDecChunk, npos - c * kDecChunk);
-    const int d = t % hd, hstep = kDecChunk / hd;
-    const T* vbase = vc + ((int64_t)b * max_seq + (int64_t)c * kDecChunk) * hd + d;
-    for (int j = t / hd; j < H; j += hstep) {
-        float acc = 0.f;
+    for (int idx = t; idx < H * hd; idx += kDecThreads) {
+        const int j = idx / hd, d = idx - j * hd;
         const float* pj = ps + j * kDecChunk;
-        for (int u = 0; u < cnt; ++u) acc = fmaf(pj[u], Elt<T>::ld(vbase + (int64_t)u * hd), acc);
+        const T* vd = vs + d;
+        float acc = 0.f;
+        for (int u = 0; u < cnt; ++u) acc = fmaf(pj[u], Elt<T>::ld(vd + u * hd), acc);
         part_o[(slot * H + j) * hd + d] = acc;
     }
 }
 
-// o[b][j*hd + d] = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c
+// o[b][j*hd + d] = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c; one
+// workgroup per (token b, head j), one thread per d
 template <typename T>
-__global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void k_decode_combine(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         int nch, int H, int hd,
                                                         T* __restrict__ o) {
-    const int b = blockIdx.x;
-    for (int e = threadIdx.x; e < H * hd; e += 256) {
-        const int j = e / hd, d = e % hd;
-        float M = -INFINITY;
-        for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(((int64_t)b * nch + c) * H + j) * 2]);
-        float L = 0.f, acc = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const int64_t sl = ((int64_t)b * nch + c) * H + j;
-            const float wgt = expf(part_ml[sl * 2] - M);
-            L = fmaf(wgt, part_ml[sl * 2 + 1], L);
-            acc = fmaf(wgt, part_o[sl * hd + d], acc);
-        }
-        Elt<T>::st(o + (int64_t)b * H * hd + e, acc / L);
+    const int b = blockIdx.x, j = blockIdx.y, d = threadIdx.x;
+    if (d >= hd) return;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, part_ml[(((int64_t)b * nch + c) * H + j) * 2]);
+    float L = 0.f, acc = 0.f;
+    for (int c = 0; c < nch; ++c) {
+        const int64_t sl = ((int64_t)b * nch + c) * H + j;
+        const float wgt = expf(part_ml[sl * 2] - M);
+        L = fmaf(wgt, part_ml[sl * 2 + 1], L);
+        acc = fmaf(wgt, part_o[sl * hd + d], acc);
     }
+    Elt<T>::st(o + ((int64_t)b * H + j) * hd + d, acc / L);
 }
 
 // keys and values of prefill positions into the cache: token n = b*t0 + t
@@ -291,30 +335,51 @@ __global__ __launch_bounds__(256) void k_softcap_rows(float* __restrict__ z, int
 
 }  // namespace
 
+// k slices of a B-row product: enough workgroups to keep every compute unit
+// streaming (about 512), each slice at least 256 of k (K / S a multiple of 64)
+int gemv_splits(int N, int K) {
+    const int wgs = (int)ceil_div(N, kGvRows);
+    int best = 1;
+    for (int sl = 2; sl <= 32; ++sl) {
+        if (K % (64 * sl) || K / sl < 256) continue;
+        if ((int64_t)wgs * sl > 1024) break;
+        best = sl;
+        if (wgs * sl >= 512) break;
+    }
+    return best;
+}
+
+template <int MODE>
+hipError_t launch_gemv(const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
+                       const float* rs, const bf16_t* aux, void* y, int64_t ldy, float* part,
+                       int S, hipStream_t s) {
+    hipLaunchKernelGGL(k_gemv_mfma<MODE>, dim3((unsigned)ceil_div(N, kGvRows), S),
+                       dim3(kGvThreads), 0, s, x, ldx, B, W, N, K, rs, aux, y, ldy, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    hipLaunchKernelGGL(k_gemv_reduce<MODE>, dim3((unsigned)ceil_div((int64_t)B * N, 256)),
+                       dim3(256), 0, s, part, S, B, N, rs, aux, y, ldy);
+    return hipGetLastError();
+}
+
 hipError_t gemv(int mode, const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
-                const float* rs, const bf16_t* aux, void* y, int64_t ldy, hipStream_t s) {
+                const float* rs, const bf16_t* aux, void* y, int64_t ldy, float* part,
+                size_t part_elems, hipStream_t s) {
     if (B < 1 || B > 32 || K % 64 || N < 1) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ceil_div(N, kGvRows));
+    int S = gemv_splits(N, K);
+    if ((size_t)S * B * N > part_elems || !part) S = 1;
     switch (mode) {
         case EPI_STORE_F32:
-            hipLaunchKernelGGL(k_gemv_mfma<EPI_STORE_F32>, grid, dim3(kGvThreads), 0, s, x, ldx,
-                               B, W, N, K, rs, aux, y, ldy);
-            break;
+            return launch_gemv<EPI_STORE_F32>(x, ldx, B, W, N, K, rs, aux, y, ldy, part, S, s);
         case EPI_ROWSCALE:
-            hipLaunchKernelGGL(k_gemv_mfma<EPI_ROWSCALE>, grid, dim3(kGvThreads), 0, s, x, ldx, B,
-                               W, N, K, rs, aux, y, ldy);
-            break;
+            return launch_gemv<EPI_ROWSCALE>(x, ldx, B, W, N, K, rs, aux, y, ldy, part, S, s);
         case EPI_ROWSCALE_RELU2:
-            hipLaunchKernelGGL(k_gemv_mfma<EPI_ROWSCALE_RELU2>, grid, dim3(kGvThreads), 0, s, x,
-                               ldx, B, W, N, K, rs, aux, y, ldy);
-            break;
+            return launch_gemv<EPI_ROWSCALE_RELU2>(x, ldx, B, W, N, K, rs, aux, y, ldy, part, S,
+                                                   s);
         case EPI_RESID:
-            hipLaunchKernelGGL(k_gemv_mfma<EPI_RESID>, grid, dim3(kGvThreads), 0, s, x, ldx, B, W,
-                               N, K, rs, aux, y, ldy);
-            break;
+            return launch_gemv<EPI_RESID>(x, ldx, B, W, N, K, rs, aux, y, ldy, part, S, s);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <typename T>
@@ -331,14 +396,14 @@ int decode_chunks(int npos) { return (int)ceil_div(npos, kDecChunk); }
 template <typename T>
 hipError_t decode_attn(const float* q, const T* kc, const T* vc, int max_seq, int npos, int B,
                        int H, int hd, float* part_o, float* part_ml, T* o, hipStream_t s) {
-    if (H > kMaxHeads || hd > 128 || kDecChunk % hd) return hipErrorInvalidValue;
+    if (H > kMaxHeads || hd > 128 || hd % 16) return hipErrorInvalidValue;
     const int nch = decode_chunks(npos);
-    hipLaunchKernelGGL(k_decode_attn<T>, dim3(nch, B), dim3(kDecChunk), 0, s, q, kc, vc, max_seq,
+    hipLaunchKernelGGL(k_decode_attn<T>, dim3(nch, B), dim3(kDecThreads), 0, s, q, kc, vc, max_seq,
                        npos, H, hd, 1.f / sqrtf((float)hd), nch, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_decode_combine<T>, dim3(B), dim3(256), 0, s, part_o, part_ml, nch, H, hd,
-                       o);
+    hipLaunchKernelGGL(k_decode_combine<T>, dim3(B, H), dim3(128), 0, s, part_o, part_ml, nch, H,
+                       hd, o);
     return hipGetLastError();
 }
 

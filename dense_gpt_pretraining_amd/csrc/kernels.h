@@ -155,8 +155,12 @@ hipError_t transpose(const T* in, int rows, int cols, int64_t ld_in, T* out,
 // y[b][n] = epi(sum_k x[b][k] W[n][k]) for B <= 32 rows (W [N][K], K a
 // multiple of 64): mode EPI_ROWSCALE, EPI_ROWSCALE_RELU2, EPI_RESID (aux
 // [B][N] with ld ldy) into bf16 y, or EPI_STORE_F32 for fp32 y = rs[b] * acc.
+// part: fp32 scratch of part_elems for a k-split (gemv_splits(N, K) * B * N
+// elements; with less, the product runs unsplit)
 hipError_t gemv(int mode, const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
-                const float* rs, const bf16_t* aux, void* y, int64_t ldy, hipStream_t s);
+                const float* rs, const bf16_t* aux, void* y, int64_t ldy, float* part,
+                size_t part_elems, hipStream_t s);
+int gemv_splits(int N, int K);
 // rotary at position pos + QK-norm of B tokens' qkv rows ([B][(H+2) hd], row
 // stride ldq): query heads into q_out fp32 [B][H][hd], the key head and the
 // value head into cache row pos of kc, vc ([B][max_seq][hd])

@@ -606,7 +606,8 @@ int scratch_for_current_device(void** out) {
 
 // Decode workspace for B tokens and a cache of max_seq positions.
 struct DecPlan {
-    size_t x0, x1, xm, r, qkv, q, o, g, part_o, part_ml, cos_t, sin_t, bytes = 0;
+    size_t x0, x1, xm, r, qkv, q, o, g, part_o, part_ml, cos_t, sin_t, gpart, bytes = 0;
+    size_t gpart_elems = 0;
 };
 
 DecPlan make_dec_plan(const nc_config& c, int max_seq) {
@@ -628,6 +629,15 @@ DecPlan make_dec_plan(const nc_config& c, int max_seq) {
     d.part_ml = take(B * nch * H * 2 * 4);
     d.cos_t = take((size_t)max_seq * (hd / 2) * 4);
     d.sin_t = take((size_t)max_seq * (hd / 2) * 4);
+    // k-slice sums of the B-row products (bf16 path)
+    if (c.dtype == NC_BF16) {
+        const int64_t Wq = (H + 2) * hd;
+        const int64_t shapes[4][2] = {{Wq, D}, {D, H * hd}, {F, D}, {D, F}};
+        for (const auto& nk : shapes)
+            d.gpart_elems = std::max<size_t>(
+                d.gpart_elems, (size_t)nc::gemv_splits((int)nk[0], (int)nk[1]) * B * nk[0]);
+    }
+    d.gpart = take(d.gpart_elems * 4);
     d.bytes = off;
     return d;
 }
@@ -661,9 +671,10 @@ int check_infer(const nc_config* cfg, int max_seq) {
 // core kernel for bf16, the SIMT product for fp32 (logits: EPI_STORE_F32)
 template <typename T>
 hipError_t dec_gemm(int mode, const T* x, int64_t ldx, int B, const T* W, int N, int K,
-                    const float* rs, const T* aux, void* y, int64_t ldy, hipStream_t s) {
+                    const float* rs, const T* aux, void* y, int64_t ldy, hipStream_t s,
+                    float* part = nullptr, size_t part_elems = 0) {
     if constexpr (std::is_same<T, nc::bf16_t>::value) {
-        return nc::gemv(mode, x, ldx, B, W, N, K, rs, aux, y, ldy, s);
+        return nc::gemv(mode, x, ldx, B, W, N, K, rs, aux, y, ldy, part, part_elems, s);
     } else {
         nc::Epilogue e;
         e.mode = mode == nc::EPI_STORE_F32 ? nc::EPI_ROWSCALE : mode;
@@ -690,6 +701,8 @@ int decode_step(const nc_config& c, const T* params, const int32_t* tok, int pos
     const T* Wt = params;
     auto Wl = [&](int l, int k) { return Wt + lay[1 + 6 * l + k].offset; };
     const int64_t per = (int64_t)B * max_seq * hd;
+    float* gp = reinterpret_cast<float*>(ws + d.gpart);
+    const size_t gpe = d.gpart_elems;
     NC_TRY(nc::rope_tables(pos + 1, hd, c.rope_base, cos_t, sin_t, s));
     T* x = P(d.x0);
     T* xn = P(d.x1);
@@ -700,18 +713,19 @@ int decode_step(const nc_config& c, const T* params, const int32_t* tok, int pos
         T* vc = cache + (2 * l + 1) * per;
         NC_TRY(nc::rms_stats<T>(x, B, D, eps, r, s));
         NC_TRY(dec_gemm<T>(nc::EPI_ROWSCALE, x, D, B, Wl(l, 0), Wq, D, r, nullptr, P(d.qkv), Wq,
-                           s));
+                           s, gp, gpe));
         NC_TRY(nc::decode_rope<T>(P(d.qkv), Wq, B, H, hd, pos, cos_t, sin_t, eps, q, kc, vc,
                                   max_seq, s));
         NC_TRY(nc::decode_attn<T>(q, kc, vc, max_seq, pos + 1, B, H, hd,
                                   reinterpret_cast<float*>(ws + d.part_o),
                                   reinterpret_cast<float*>(ws + d.part_ml), P(d.o), s));
         NC_TRY(dec_gemm<T>(nc::EPI_RESID, P(d.o), H * hd, B, Wl(l, 3), D, H * hd, nullptr, x, xm,
-                           D, s));
+                           D, s, gp, gpe));
         NC_TRY(nc::rms_stats<T>(xm, B, D, eps, r, s));
         NC_TRY(dec_gemm<T>(nc::EPI_ROWSCALE_RELU2, xm, D, B, Wl(l, 4), F, D, r, nullptr, P(d.g),
-                           F, s));
-        NC_TRY(dec_gemm<T>(nc::EPI_RESID, P(d.g), F, B, Wl(l, 5), D, F, nullptr, xm, xn, D, s));
+                           F, s, gp, gpe));
+        NC_TRY(dec_gemm<T>(nc::EPI_RESID, P(d.g), F, B, Wl(l, 5), D, F, nullptr, xm, xn, D, s, gp,
+                           gpe));
         std::swap(x, xn);
     }
     NC_TRY(nc::rms_stats<T>(x, B, D, eps, r, s));

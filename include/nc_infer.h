@@ -72,7 +72,7 @@ int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* toke
  * every GPU it runs on until the process ends, instead of a `ws` argument.
  * Its kernels are nc_decode_step's and the results are bitwise the same.
  * NC_ERR_WORKSPACE when the step needs more than 32 MiB (nc_infer_workspace_
- * size(cfg, max_seq, 0) > 32 MiB; the depth-20 shapes need about 11 MiB at
+ * size(cfg, max_seq, 0) > 32 MiB; the depth-20 shapes need about 18 MiB at
  * batch 32 and max_seq 8192).  The array holds the last call's values (the
  * step writes every byte it reads); calls that overlap on one GPU, on any
  * streams, race on it.

@@ -34,10 +34,12 @@ def _case(name, over, t0, positions, max_seq):
 
 
 def test_no_alloc_decode_matches_the_workspace_decode_on_two_calls():
-    # first call: bf16, 8 sequences, a 512-position cache after a prefill
-    _case("d20", dict(n_layer=2, batch=8), 256, [256, 257, 300], 512)
+    # first call: bf16, 8 sequences, a 512-position cache after a prefill;
+    # every position after the prompt is decoded in turn (the cache must hold
+    # the sequence so far)
+    _case("d20", dict(n_layer=2, batch=8), 256, list(range(256, 301)), 512)
     # second call, smaller: 2 sequences, one layer, 128 positions, from empty
-    _case("d20", dict(n_layer=1, batch=2), 0, [0, 1, 2, 63], 128)
+    _case("d20", dict(n_layer=1, batch=2), 0, list(range(0, 64)), 128)
 
 
 def test_no_alloc_decode_refuses_workspaces_beyond_the_array():
