@@ -113,6 +113,9 @@ _sigs = {
     "nc_op_matmul": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P, C.c_int64,
                                C.c_int32, _P, C.c_int64, C.c_int32, _P, C.c_int64, _P,
                                C.c_size_t, _P]),
+    "nc_op_matmul_epilogue": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int32, _P,
+                                        C.c_int64, C.c_int32, _P, C.c_int64, C.c_int32, _P,
+                                        C.c_int64, C.c_int32, _P, _P, _P]),
     "nc_op_attention_fwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
                                                           _P]),
     "nc_op_attention_bwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
@@ -305,6 +308,13 @@ def nc_op_matmul(dtype, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cp, ldc, ws
                  stream):
     _check("nc_op_matmul", _lib.nc_op_matmul(dtype, M, N, K, A, lda, int(a_kmajor), B, ldb,
                                              int(b_kmajor), Cp, ldc, ws, ws_bytes, stream))
+
+
+def nc_op_matmul_epilogue(dtype, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cp, ldc, mode,
+                          rowscale, aux, stream):
+    _check("nc_op_matmul_epilogue", _lib.nc_op_matmul_epilogue(
+        dtype, M, N, K, A, lda, int(a_kmajor), B, ldb, int(b_kmajor), Cp, ldc, mode, rowscale, aux,
+        stream))
 
 
 def nc_op_attention_fwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, lse, stream):

@@ -273,6 +273,10 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
 // output stores are marked non-temporal: the product never reads its output
 // back, and streaming it past L2 keeps the operand panels that neighbouring
 // tiles share resident (measured faster over the whole step)
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+// cache-policy operand of the buffer stores: non-temporal
+constexpr int kNonTemporal = 2;
 __device__ __forceinline__ void st_nt(void* p, uint2 v) {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(__builtin_bit_cast(u32x2, v), (u32x2*)p);
@@ -692,6 +696,73 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mfma(int M, int N, int K, 
     bf16_t* const stage_arr = wave < 2 ? ldsA0 : wave < 4 ? ldsA1 : wave < 6 ? ldsB0 : ldsB1;
     float* stage = reinterpret_cast<float*>(stage_arr) + (wave & 1) * 4096;
     constexpr bool kRs = MODE == EPI_ROWSCALE || MODE == EPI_ROWSCALE_RELU2 || MODE == EPI_RELU2_BWD;
+    // Whole tiles (every tile of the step's shapes but the ragged edges) take
+    // a branch-free path: buffer loads and stores whose row offsets are scalar
+    // multiples of the row stride, so a row costs no address arithmetic and
+    // the 16 LDS reads of a pass are not serialised behind bounds tests.  Byte
+    // offsets inside a tile must fit in 31 bits.
+    constexpr int kEs = MODE == EPI_STORE_F32 ? 4 : 2;
+    const bool fast = MODE != EPI_QKV_ROPE && full_n && m0 + kTM <= M && ldc <= (1 << 20) &&
+                      !(MODE == EPI_STORE_F32 && e.accumulate);
+    if (fast) {
+        const int64_t tile0 = (int64_t)m0 * ldc + n0;
+        const buf_rsrc_t rc = make_rsrc(static_cast<char*>(C) + tile0 * kEs);
+        const int srow = 2 * (int)ldc * kEs;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row0 = wm * 64 + 32 * j + hi;
+            const int voff = (row0 * (int)ldc + wn * 128 + 4 * li) * kEs;
+            // the pass's epilogue inputs are requested before the LDS round trip
+            u32x2_t auxv[16];
+            float rsv[16];
+            if (kAux) {
+                const buf_rsrc_t ra = make_rsrc(static_cast<const bf16_t*>(e.aux) + tile0);
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    auxv[t] = __builtin_amdgcn_raw_buffer_load_b64(ra, voff, t * srow, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) rsv[t] = kRs ? lds_rs[row0 + 2 * t] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 8 * i + 2 * q + hi;
+                    *reinterpret_cast<float4*>(stage + li * 128 + ((c ^ li) << 2)) =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]);
+                }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int row = 2 * t + hi;
+                const float4 v = *reinterpret_cast<const float4*>(stage + row * 128 + ((li ^ row) << 2));
+                if (MODE == EPI_STORE_F32) {
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rc, voff,
+                                                           t * srow, kNonTemporal);
+                    continue;
+                }
+                float o[4] = {v.x, v.y, v.z, v.w};
+                const float x[4] = {bf_lo(auxv[t].x), bf_hi(auxv[t].x), bf_lo(auxv[t].y),
+                                    bf_hi(auxv[t].y)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (MODE == EPI_RESID) o[q] += x[q];
+                    if (MODE == EPI_AXPBY) o[q] = e.alpha * x[q] + e.beta * o[q];
+                    if (MODE == EPI_RELU2_BWD) o[q] *= 2.f * rsv[t] * __builtin_amdgcn_sqrtf(x[q]);
+                    if (MODE == EPI_ROWSCALE) o[q] *= rsv[t];
+                    if (MODE == EPI_ROWSCALE_RELU2) {
+                        const float u = fmaxf(rsv[t] * o[q], 0.f);
+                        o[q] = u * u;
+                    }
+                }
+                const u32x2_t w = {pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(w, rc, voff, t * srow, kNonTemporal);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         // the pass's epilogue inputs are requested before the LDS round trip

@@ -4,6 +4,11 @@
 #include "../../include/nc_ops.h"
 #include "kernels.h"
 
+static_assert(NC_EPI_ROWSCALE == nc::EPI_ROWSCALE && NC_EPI_ROWSCALE_RELU2 == nc::EPI_ROWSCALE_RELU2 &&
+                  NC_EPI_RESID == nc::EPI_RESID && NC_EPI_RELU2_BWD == nc::EPI_RELU2_BWD &&
+                  NC_EPI_STORE == nc::EPI_STORE_T,
+              "the unit ABI's epilogue codes are the library's modes");
+
 namespace {
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -44,6 +49,43 @@ int nc_op_matmul(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
                                     a_kmajor != 0, static_cast<const nc::bf16_t*>(B), ldb,
                                     b_kmajor != 0, C, ldc, e, static_cast<float*>(ws), ws_bytes,
                                     s));
+}
+
+int nc_op_matmul_epilogue(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A,
+                          int64_t lda, int32_t a_kmajor, const void* B, int64_t ldb,
+                          int32_t b_kmajor, void* C, int64_t ldc, int32_t mode,
+                          const float* rowscale, const void* aux, void* stream) {
+    if (dtype != NC_F32 && dtype != NC_BF16) return NC_ERR_DTYPE;
+    if (M < 1 || N < 1 || K < 1) return NC_ERR_CONFIG;
+    if (mode < NC_EPI_ROWSCALE || mode > NC_EPI_STORE) return NC_ERR_CONFIG;
+    const bool need_rs = mode == NC_EPI_ROWSCALE || mode == NC_EPI_ROWSCALE_RELU2 ||
+                         mode == NC_EPI_RELU2_BWD;
+    const bool need_aux = mode == NC_EPI_RESID || mode == NC_EPI_RELU2_BWD;
+    if (!A || !B || !C || (need_rs && !rowscale) || (need_aux && !aux)) return NC_ERR_NULL;
+    if (!al16(A) || !al16(B) || !al16(C) || (aux && !al16(aux))) return NC_ERR_ALIGN;
+    if (ldc < N) return NC_ERR_CONFIG;
+    if (a_kmajor ? lda < K : lda < M) return NC_ERR_CONFIG;
+    if (b_kmajor ? ldb < K : ldb < N) return NC_ERR_CONFIG;
+    nc::Epilogue e;
+    e.mode = mode;   // the NC_EPI_* values are the library's epilogue modes
+    e.rowscale = need_rs ? rowscale : nullptr;
+    e.aux = need_aux ? aux : nullptr;
+    if (dtype == NC_F32) {
+        hipStream_t s = nc::enqueue_stream(stream);
+        return ret(nc::gemm<float>(M, N, K, static_cast<const float*>(A), lda, a_kmajor != 0,
+                                   static_cast<const float*>(B), ldb, b_kmajor != 0, C, ldc, e,
+                                   nullptr, 0, s));
+    }
+    // the bf16 products the step runs: (k, k) with every mode, (k, mn) with
+    // the data-gradient modes
+    if (!a_kmajor) return NC_ERR_UNSUPPORTED;
+    if (!b_kmajor && mode != NC_EPI_STORE && mode != NC_EPI_RELU2_BWD) return NC_ERR_UNSUPPORTED;
+    if (K % 64 || lda % 8 || ldb % 8 || ldc % 4) return NC_ERR_UNSUPPORTED;
+    if (!b_kmajor && ldb < ((N + 7) / 8) * 8) return NC_ERR_UNSUPPORTED;
+    hipStream_t s = nc::enqueue_stream(stream);
+    return ret(nc::gemm<nc::bf16_t>(M, N, K, static_cast<const nc::bf16_t*>(A), lda, true,
+                                    static_cast<const nc::bf16_t*>(B), ldb, b_kmajor != 0, C, ldc,
+                                    e, nullptr, 0, s));
 }
 
 static int attn_check(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd, int64_t ldq,

@@ -35,6 +35,26 @@ int nc_op_matmul(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A, 
                  int64_t ldc, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The bias-free linear layers' products with their fused epilogues, stored
+ * as T in C [M, ldc] (same operand conventions as nc_op_matmul):
+ *   NC_EPI_ROWSCALE        C = rowscale[m] * acc          (a normed input, n(x) W^T)
+ *   NC_EPI_ROWSCALE_RELU2  C = relu(rowscale[m] * acc)^2  (the MLP's first layer)
+ *   NC_EPI_RESID           C = aux[m][n] + acc            (a residual add)
+ *   NC_EPI_RELU2_BWD       C = rowscale[m] * acc * 2 sqrt(aux[m][n])
+ *                          (aux = relu(u)^2; the relu^2 derivative)
+ *   NC_EPI_STORE           C = acc
+ * rowscale fp32 [M]; aux T [M, ldc].  bf16 runs the (k-major, k-major) pair
+ * with every mode and (k-major, mn-major) with NC_EPI_RELU2_BWD and
+ * NC_EPI_STORE, K a multiple of 64; fp32 runs every pair.
+ */
+enum { NC_EPI_ROWSCALE = 1, NC_EPI_ROWSCALE_RELU2 = 2, NC_EPI_RESID = 3, NC_EPI_RELU2_BWD = 4,
+       NC_EPI_STORE = 5 };
+int nc_op_matmul_epilogue(int32_t dtype, int32_t M, int32_t N, int32_t K, const void* A,
+                          int64_t lda, int32_t a_kmajor, const void* B, int64_t ldb,
+                          int32_t b_kmajor, void* C, int64_t ldc, int32_t mode,
+                          const float* rowscale, const void* aux, void* stream);
+
+/*
  * Causal multi-query attention (one shared K/V head; architecture list of the
  * nanochat article).  q: T [B*T, H, hd] with token stride ldq (elements);
  * k, v: T [B*T, hd] with token stride ldkv; o: T [B*T, H*hd];

@@ -249,3 +249,60 @@ def test_rope_qknorm(dtype, hd):
     assert rel_l2(got[:, :, :H + 1], nrm) < tol
     np.testing.assert_array_equal(got[:, :, H + 1], xs[:, :, H + 1])
     assert rel_l2(from_dev(rqk).reshape(Bn, T, H + 1), r[..., 0]) < 1e-5
+
+
+_EPI = {"rowscale": 1, "relu2": 2, "resid": 3, "relu2_bwd": 4, "store": 5}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", list(_EPI))
+@pytest.mark.parametrize("M,N,K,b_kmajor", [
+    (300, 520, 192, True),      # ragged m and n tails over several tiles
+    (512, 1280, 1280, True),    # whole tiles, the d20 K
+    (65, 136, 128, True),       # one partial tile
+    (300, 520, 192, False),     # weight read as stored (data-gradient layout)
+])
+def test_matmul_epilogue(dtype, mode, M, N, K, b_kmajor):
+    """Each fused epilogue of the linear layers against its definition on
+    the float64 product: bf16 outputs are rounded once (rel-L2 bar 1e-2),
+    fp32 within 1e-5."""
+    torch = require_gpu()
+    b = _b()
+    if dtype == "bf16" and not b_kmajor and mode not in ("store", "relu2_bwd"):
+        pytest.skip("the step runs the mn-major weight layout only in its data gradients")
+    A = rand((M, K), 11, dtype=dtype)
+    W = rand((N, K), 12, scale=0.05, dtype=dtype)
+    rng = np.random.default_rng(13)
+    rs = (0.5 + rng.random(M)).astype(np.float32)
+    aux = rand((M, N), 14, dtype=dtype)
+    if mode == "relu2_bwd":
+        aux = np.square(aux)
+        if dtype == "bf16":
+            from nc_synth import bf16_round
+            aux = bf16_round(aux.astype(np.float32))
+    acc = A.astype(np.float64) @ W.astype(np.float64).T
+    want = {"rowscale": lambda: rs[:, None] * acc,
+            "relu2": lambda: np.maximum(rs[:, None] * acc, 0) ** 2,
+            "resid": lambda: aux.astype(np.float64) + acc,
+            "relu2_bwd": lambda: rs[:, None] * acc * 2 * np.sqrt(aux.astype(np.float64)),
+            "store": lambda: acc}[mode]()
+    np_ = -(-N // 8) * 8
+    if b_kmajor:
+        Bd, ldb = to_dev(W, dtype), K
+    else:
+        Wt = np.zeros((K, np_), np.float32)
+        Wt[:, :N] = W.T
+        Bd, ldb = to_dev(Wt, dtype), np_
+    ldc = np_
+    auxp = np.zeros((M, ldc), np.float32)
+    auxp[:, :N] = aux
+    auxd = to_dev(auxp, dtype)
+    Cd = to_dev(np.full((M, ldc), np.nan, np.float32), dtype)
+    rsd = torch.from_numpy(rs).cuda()
+    b.nc_op_matmul_epilogue(DT[dtype], M, N, K, to_dev(A, dtype).data_ptr(), K, True,
+                            Bd.data_ptr(), ldb, b_kmajor, Cd.data_ptr(), ldc, _EPI[mode],
+                            rsd.data_ptr(), auxd.data_ptr(), stream())
+    torch.cuda.synchronize()
+    got = from_dev(Cd)[:, :N]
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, want) < (1e-2 if dtype == "bf16" else 1e-5), (mode, rel_l2(got, want))
