@@ -117,7 +117,7 @@ _sigs = {
                                         C.c_int64, C.c_int32, _P, C.c_int64, C.c_int32, _P,
                                         C.c_int64, C.c_int32, _P, _P, _P]),
     "nc_op_attention_fwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
-                                                          _P]),
+                                                          C.c_int32, _P]),
     "nc_op_attention_bwd": (C.c_int, [C.c_int32] * 5 + [_P, _P, _P, C.c_int64, C.c_int64, _P, _P,
                                                           _P, _P, C.c_size_t, _P, _P, _P, _P]),
     "nc_op_attention_bwd_scratch_bytes": (C.c_int, [C.c_int32] * 4 + [C.POINTER(C.c_size_t)]),
@@ -317,9 +317,9 @@ def nc_op_matmul_epilogue(dtype, M, N, K, A, lda, a_kmajor, B, ldb, b_kmajor, Cp
         stream))
 
 
-def nc_op_attention_fwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, lse, stream):
+def nc_op_attention_fwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, lse, stream, qk_normed=0):
     _check("nc_op_attention_fwd", _lib.nc_op_attention_fwd(dtype, B, T, H, hd, q, k, v, ldq,
-                                                           ldkv, o, lse, stream))
+                                                           ldkv, o, lse, qk_normed, stream))
 
 
 def nc_op_attention_bwd(dtype, B, T, H, hd, q, k, v, ldq, ldkv, o, dout, lse, scratch,

@@ -150,11 +150,16 @@ __device__ __forceinline__ void copy_kv_tile(const char* kg, const char* vg, int
 }
 
 // ------------------------------------------------------------------ forward
-template <int HD>
+// FIXED: the caller guarantees |q . k| scale_log2 <= m_fixed for every pair
+// (QK-norm bounds every score), so the softmax subtracts the constant m_fixed
+// instead of a running maximum: the result is the same softmax (it is
+// shift-invariant), every exponent lies in [-2 m_fixed, 0], and the per-score
+// maximum, its lane exchange and the rescaling test drop out.
+template <int HD, bool FIXED>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     int64_t ldq, int64_t ldkv, bf16_t* __restrict__ o, float* __restrict__ lse, int B, int T,
-    int H, float scale_log2) {
+    int H, float scale_log2, float m_fixed) {
     constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
     // two buffers of a K tile and a V tile, as four distinct arrays: with the
     // buffer known at compile time (the key loop is unrolled by two) and one
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     f32x16_t oacc[HD / 32];
 #pragma unroll
     for (int db = 0; db < HD / 32; ++db) oacc[db] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = FIXED ? m_fixed : -INFINITY, l_run = 0.f;
 
     issue(0, sK0, sV0);
     // key tile it from (sK, sV); the next one is copied into (nK, nV)
@@ -231,20 +236,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
                     if (key > t) s[bi][rr] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        if (!FIXED) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[bi][rr]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mc = mx * scale_log2;
-        if (__ballot(mc > m_run + kLazy)) {
-            const float mn = fmaxf(m_run, mc);
-            const float alpha = ex2(m_run - mn);
-            l_run *= alpha;
+                for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[bi][rr]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mc = mx * scale_log2;
+            if (__ballot(mc > m_run + kLazy)) {
+                const float mn = fmaxf(m_run, mc);
+                const float alpha = ex2(m_run - mn);
+                l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < HD / 32; ++db) oacc[db] *= alpha;
-            m_run = mn;
+                for (int db = 0; db < HD / 32; ++db) oacc[db] *= alpha;
+                m_run = mn;
+            }
         }
         float ps = 0.f;
 #pragma unroll
@@ -935,11 +942,21 @@ int chunk_rows(int B, int T, int H) {
 
 template <int HD>
 hipError_t launch_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
-                      int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, hipStream_t s) {
+                      int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, hipStream_t s,
+                      bool qk_normed) {
     const int n_rb = (T * H + kRB - 1) / kRB;
     const float scale_log2 = kLog2e / sqrtf((float)HD);
-    hipLaunchKernelGGL(k_attn_fwd_mfma<HD>, dim3(n_rb * B), dim3(256), 0, s, q, k, v, ldq, ldkv,
-                       o, lse, B, T, H, scale_log2);
+    if (qk_normed) {
+        // RMS-normalised heads have norm sqrt(hd) (each bf16 element is within
+        // 2^-9 of it), so |q . k| scale_log2 <= sqrt(hd) log2 e (1 + 2^-9)^2;
+        // the offset leaves 6% headroom above that
+        const float m_fixed = sqrtf((float)HD) * kLog2e * 1.0625f;
+        hipLaunchKernelGGL((k_attn_fwd_mfma<HD, true>), dim3(n_rb * B), dim3(256), 0, s, q, k, v,
+                           ldq, ldkv, o, lse, B, T, H, scale_log2, m_fixed);
+    } else {
+        hipLaunchKernelGGL((k_attn_fwd_mfma<HD, false>), dim3(n_rb * B), dim3(256), 0, s, q, k,
+                           v, ldq, ldkv, o, lse, B, T, H, scale_log2, 0.f);
+    }
     return hipGetLastError();
 }
 
@@ -1030,9 +1047,9 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
 
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,
-                         hipStream_t s) {
-    if (hd == 128) return launch_fwd<128>(q, k, v, ldq, ldkv, o, lse, B, T, H, s);
-    if (hd == 64) return launch_fwd<64>(q, k, v, ldq, ldkv, o, lse, B, T, H, s);
+                         hipStream_t s, bool qk_normed) {
+    if (hd == 128) return launch_fwd<128>(q, k, v, ldq, ldkv, o, lse, B, T, H, s, qk_normed);
+    if (hd == 64) return launch_fwd<64>(q, k, v, ldq, ldkv, o, lse, B, T, H, s, qk_normed);
     return hipErrorInvalidValue;
 }
 
@@ -1054,8 +1071,8 @@ hipError_t attn_bwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int6
 template <>
 hipError_t attn_fwd<bf16_t>(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                             int64_t ldkv, bf16_t* o, float* lse, int B, int Tn, int H, int hd,
-                            hipStream_t s) {
-    return attn_fwd_mfma(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
+                            hipStream_t s, bool qk_normed) {
+    return attn_fwd_mfma(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s, qk_normed);
 }
 
 template <>

@@ -213,7 +213,7 @@ hipError_t attn_bwd_simt(const T* q, const T* k, const T* v, int64_t ldq, int64_
 template <>
 hipError_t attn_fwd<float>(const float* q, const float* k, const float* v, int64_t ldq,
                            int64_t ldkv, float* o, float* lse, int B, int Tn, int H, int hd,
-                           hipStream_t s) {
+                           hipStream_t s, bool) {
     return attn_fwd_simt<float>(q, k, v, ldq, ldkv, o, lse, B, Tn, H, hd, s);
 }
 

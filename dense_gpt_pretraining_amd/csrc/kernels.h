@@ -63,9 +63,11 @@ size_t gemm_splitk_bytes(int M, int N, int K);
 // attn_fwd / attn_bwd below run the per-row kernels of attn_simt.hip for
 // float and the matrix-core kernels for bf16.
 // Matrix-core kernels (bf16, T a multiple of 64, hd 64 or 128).
+// qk_normed: q and k heads are RMS-normalised (QK-norm), which bounds every
+// score and lets the bf16 forward drop its running maximum
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,
-                         hipStream_t s);
+                         hipStream_t s, bool qk_normed = false);
 // Tail of the step's attention backward fused into the bf16 kernels: instead
 // of fp32 dq, dk, dv they write dqkv (bf16, same layout and stride as qkv) =
 // r1[token] times, for the query heads and the key head, the backward of
@@ -94,7 +96,7 @@ size_t attn_bwd_scratch_bytes(int B, int T, int H, int hd);
 template <typename T>
 hipError_t attn_fwd(const T* q, const T* k, const T* v, int64_t ldq,
                     int64_t ldkv, T* o, float* lse, int B, int Tn, int H,
-                    int hd, hipStream_t s);
+                    int hd, hipStream_t s, bool qk_normed = false);
 // Backward: dq [B*T, H, hd], dk, dv [B*T, hd], all fp32; scratch holds
 // attn_bwd_scratch_bytes(B, T, H, hd) bytes.
 template <typename T>

@@ -100,7 +100,7 @@ static int attn_check(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd
 
 int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
                         const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
-                        void* o, float* lse, void* stream) {
+                        void* o, float* lse, int32_t qk_normed, void* stream) {
     int rc = attn_check(dtype, B, T, H, hd, ldq, ldkv);
     if (rc != NC_OK) return rc;
     if (!q || !k || !v || !o || !lse) return NC_ERR_NULL;
@@ -113,7 +113,7 @@ int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t 
     return ret(nc::attn_fwd<nc::bf16_t>(
         static_cast<const nc::bf16_t*>(q), static_cast<const nc::bf16_t*>(k),
         static_cast<const nc::bf16_t*>(v), ldq, ldkv, static_cast<nc::bf16_t*>(o), lse, B, T, H,
-        hd, s));
+        hd, s, qk_normed != 0));
 }
 
 int nc_op_attention_bwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,

@@ -343,8 +343,9 @@ struct Step {
         }
         NC_RUN("attn_fwd", 4.0 * hd * H * pairs(),
                2.0 * N * H * hd * es() + 2.0 * N * hd * es() + N * H * 4.0,
+               // q and k leave QK-norm with RMS 1 per head
                nc::attn_fwd<T>(qkv, qkv + H * hd, qkv + (H + 1) * hd, Wq, Wq, O(sl), LSE(sl),
-                               c.batch, c.seq_len, (int)H, (int)hd, s));
+                               c.batch, c.seq_len, (int)H, (int)hd, s, true));
         T* xm = XM(sl);
         NC_RUN("gemm_nt_resid", gf(N, D, H * hd), gb(N, D, H * hd, es(), rowb),
                nc::gemm<T>((int)N, (int)D, (int)(H * hd), O(sl), H * hd, true, W(i_layer(l, 3)),

@@ -60,11 +60,15 @@ int nc_op_matmul_epilogue(int32_t dtype, int32_t M, int32_t N, int32_t K, const 
  * k, v: T [B*T, hd] with token stride ldkv; o: T [B*T, H*hd];
  * lse: fp32 [B*T*H], the log-sum-exp of each row's scaled scores.
  * o[t, j] = sum_{tau <= t} softmax(q[t,j].k[tau] / sqrt(hd)) v[tau].
- * hd is 64 or 128, T a multiple of 64.
+ * hd is 64 or 128, T a multiple of 64.  qk_normed nonzero promises that
+ * every q and k head has RMS 1 (QK-norm, as in the step), which bounds each
+ * scaled score by sqrt(hd) (up to bf16 rounding): the bf16 kernel then
+ * subtracts a fixed offset instead of a running maximum (same softmax).  The
+ * result is undefined when the promise does not hold; fp32 ignores the flag.
  */
 int nc_op_attention_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd,
                         const void* q, const void* k, const void* v, int64_t ldq, int64_t ldkv,
-                        void* o, float* lse, void* stream);
+                        void* o, float* lse, int32_t qk_normed, void* stream);
 
 /*
  * Backward of nc_op_attention_fwd for output gradient dout (T [B*T, H*hd]).

@@ -213,8 +213,9 @@ def test_attention_at_the_long_configuration_shape():
     base = qkv.data_ptr()
     o = torch.empty((n, H * hd), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(n * H, dtype=torch.float32, device="cuda")
+    # q and k have RMS 1 per head: the fixed-offset forward the step runs
     b.nc_op_attention_fwd(1, Bn, T, H, hd, base, base + H * hd * 2, base + (H + 1) * hd * 2, ld,
-                          ld, o.data_ptr(), lse.data_ptr(), stream())
+                          ld, o.data_ptr(), lse.data_ptr(), stream(), 1)
     dod = to_dev(do.reshape(n, H * hd), "bf16")
     nsc = b.nc_op_attention_bwd_scratch_bytes(Bn, T, H, hd)
     scratch = torch.empty(nsc, dtype=torch.uint8, device="cuda")

@@ -105,10 +105,13 @@ def _pack_qkv(q, k, v):
     return buf
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,qk_normed", [("bf16", 0), ("bf16", 1), ("f32", 0)])
 @pytest.mark.parametrize("Bn,T,H,hd", [(2, 128, 3, 64), (1, 192, 2, 128), (2, 64, 5, 128),
                                        (1, 1024, 3, 128)])
-def test_attention_forward_backward(dtype, Bn, T, H, hd):
+def test_attention_forward_backward(dtype, qk_normed, Bn, T, H, hd):
+    """q and k heads have RMS 1 (as after QK-norm), so the bf16 forward is
+    checked both with its running maximum and with the fixed offset the step
+    uses."""
     torch = require_gpu()
     b = _b()
     q, k, v = _qkv(Bn, T, H, hd, dtype, 10)
@@ -120,7 +123,8 @@ def test_attention_forward_backward(dtype, Bn, T, H, hd):
     o = torch.empty((Bn * T, H * hd), dtype=buf.dtype, device="cuda")
     lse = torch.empty(Bn * T * H, dtype=torch.float32, device="cuda")
     b.nc_op_attention_fwd(DT[dtype], Bn, T, H, hd, base, base + H * hd * es,
-                          base + (H + 1) * hd * es, ld, ld, o.data_ptr(), lse.data_ptr(), stream())
+                          base + (H + 1) * hd * es, ld, ld, o.data_ptr(), lse.data_ptr(), stream(),
+                          qk_normed)
     torch.cuda.synchronize()
     want_o = np.concatenate([oracle.causal_mqa_attention(
         q[i * T:(i + 1) * T].astype(np.float64), k[i * T:(i + 1) * T].astype(np.float64),
