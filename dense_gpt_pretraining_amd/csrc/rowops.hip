@@ -216,9 +216,10 @@ __device__ __forceinline__ float tanh_r(float y2) {
     return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y2) + 1.f);
 }
 
-// One wave per row.  The row's x and dn are read once into registers
-// (MAXC 16-byte chunks of each per lane), used for the dot product and again
-// for the output, so HBM sees each input byte once.
+// One wave per row.  The row's x, dn and residual gradient are read once into
+// registers (MAXC 16-byte chunks of x and dn per lane, and the matching fp32
+// values of dres), all requested before the row's dot product, so a row costs
+// one round trip to HBM and HBM sees each input byte once.
 template <typename T, int MAXC>
 __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     const T* __restrict__ dn, const T* __restrict__ x,
@@ -230,14 +231,24 @@ __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     if (row >= N) return;
     const T* g = dn + row * D;
     const T* xr = x + row * D;
+    float* d = dres + row * D;
     uint4 xraw[MAXC], graw[MAXC];
-    float dot = 0.f;
+    float dv[MAXC][V];
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int c = (ci * kWave + lane) * V;
         if (c < D) {
             xraw[ci] = *reinterpret_cast<const uint4*>(xr + c);
             graw[ci] = *reinterpret_cast<const uint4*>(g + c);
+#pragma unroll
+            for (int k = 0; k < V; ++k) dv[ci][k] = d[c + k];
+        }
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int ci = 0; ci < MAXC; ++ci) {
+        const int c = (ci * kWave + lane) * V;
+        if (c < D) {
             float xv[V], gv[V];
             unpack_chunk<T>(xraw[ci], xv);
             unpack_chunk<T>(graw[ci], gv);
@@ -248,7 +259,6 @@ __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     dot = wave_sum(dot);
     const float rr = r[row];
     const float coef = rr * rr * dot / (float)D;
-    float* d = dres + row * D;
     T* dt = dres_t + row * D;
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
@@ -258,7 +268,7 @@ __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
             unpack_chunk<T>(xraw[ci], xv);
             unpack_chunk<T>(graw[ci], gv);
 #pragma unroll
-            for (int k = 0; k < V; ++k) o[k] = d[c + k] + gv[k] - coef * xv[k];
+            for (int k = 0; k < V; ++k) o[k] = dv[ci][k] + gv[k] - coef * xv[k];
 #pragma unroll
             for (int k = 0; k < V; ++k) d[c + k] = o[k];
             st_vec<T>(dt + c, o);
@@ -503,6 +513,7 @@ hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D,
     }
     NC_NB_CASE(1)
     NC_NB_CASE(2)
+    NC_NB_CASE(3)
     NC_NB_CASE(4)
     NC_NB_CASE(8)
     NC_NB_CASE(16)
