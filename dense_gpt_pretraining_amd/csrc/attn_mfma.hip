@@ -299,6 +299,144 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
     }
 }
 
+// ------------------------------------------------------------------ decode
+// Attention of one new token per sequence over its key/value cache (the
+// decode step of generation).  The token's H query heads are the 32-row
+// block of the forward kernel's layout (rows >= H are zero), so the scores
+// are S^T = K Q^T with one query row per lane and the weighted values
+// O^T = V^T P^T, with the same fragment orders as the forward kernel.
+// Workgroup (chunk c, sequence b) takes keys 256 c .. +255 of the cache;
+// wave w the 64 keys 256 c + 64 w .. +63: its key fragments come straight
+// from global memory (one 16-byte read per lane and k step), its value rows
+// go to its own LDS tile and are read with the transpose read.  The heads
+// are QK-normalised, so the softmax subtracts the fixed offset m_fixed
+// (every exponent <= 0): a chunk's partial results are plain sums over its
+// keys, the four waves' sums are added in LDS in wave order, and the chunk
+// writes O_c = sum p v and l_c = sum p per head with a zero offset for the
+// combine kernel (which then divides sum_c O_c by sum_c l_c).  Keys at or
+// past npos get p = 0, and their cache rows are read as zeros.
+constexpr int kDecKeys = 256;   // keys per decode workgroup (4 waves x kKT)
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_decode_mfma(
+    const float* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    int max_seq, int npos, int H, float scale_log2, float m_fixed, int nch,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    constexpr int TB = tile_bytes(HD), NI = tile_copies(HD);
+    __shared__ __align__(1024) char sV[4 * TB];
+    const int c = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, li = lane & 31, g = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int key0 = c * kDecKeys + w * kKT;
+    char* myV = sV + w * TB;
+    // rows of this wave's keys that hold the sequence so far (positions below
+    // npos <= max_seq); the rest read zeros, so the value tile never holds the
+    // stale contents of later cache rows
+    const int rows_ok = max(0, min(kKT, npos - key0));
+    const int64_t row0 = (int64_t)b * max_seq + key0;
+    {
+        // the wave copies its whole value tile: the tile's four copy groups
+        constexpr int RPI = 1024 / (HD * 2);
+        const buf_rsrc_t rv = make_rsrc(vc + row0 * HD, rows_ok * HD * 2);
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww)
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int row = (ww * NI + i) * RPI + lane / (HD / 8);
+                const int p = lane % (HD / 8);
+                lds_copy<16>(rv, row * HD * 2 + ((p ^ swz<HD>(row)) << 4),
+                             myV + (ww * NI + i) * 1024);
+            }
+    }
+    // Q^T fragments: row li is head li of token b (zero beyond H)
+    bf16x8_t qf[HD / 16];
+    {
+        const float* qrow = q + ((int64_t)b * H + (li < H ? li : 0)) * HD;
+#pragma unroll
+        for (int kk = 0; kk < HD / 16; ++kk) {
+            float v8[8];
+            const float4 a = *reinterpret_cast<const float4*>(qrow + 16 * kk + 8 * g);
+            const float4 a2 = *reinterpret_cast<const float4*>(qrow + 16 * kk + 8 * g + 4);
+            v8[0] = a.x; v8[1] = a.y; v8[2] = a.z; v8[3] = a.w;
+            v8[4] = a2.x; v8[5] = a2.y; v8[6] = a2.z; v8[7] = a2.w;
+            qf[kk] = li < H ? pack8(v8) : as_bf16x8(make_uint4(0, 0, 0, 0));
+        }
+    }
+    // S^T of the wave's two 32-key blocks; key fragments from global memory
+    f32x16_t sc[2] = {zero16(), zero16()};
+    {
+        const buf_rsrc_t rk = make_rsrc(kc + row0 * HD, rows_ok * HD * 2);
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int kk = 0; kk < HD / 16; ++kk) {
+                const int off = ((32 * bi + li) * HD + 16 * kk + 8 * g) * 2;
+                const bf16x8_t kf = __builtin_bit_cast(
+                    bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                sc[bi] = mfma32(kf, qf[kk], sc[bi]);
+            }
+    }
+    float l_run = 0.f;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int key = key0 + 32 * bi + 8 * (rr >> 2) + 4 * g + (rr & 3);
+            const float p = key < npos ? ex2(fmaf(sc[bi][rr], scale_log2, -m_fixed)) : 0.f;
+            sc[bi][rr] = p;
+            l_run += p;
+        }
+    l_run += __shfl_xor(l_run, 32, 64);
+    // this wave's value tile has landed
+    wait_vmem();
+    f32x16_t oacc[HD / 32];
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db) oacc[db] = zero16();
+    int ld_src[NI], row_off[HD / 16], tr_off[HD / 32][2];
+    tile_lane_offsets<HD, NI>(0, lane, HD, ld_src, row_off, tr_off);
+#pragma unroll
+    for (int ks = 0; ks < kKT / 16; ++ks) {
+        const int bi = ks >> 1, h = ks & 1;
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sc[bi][8 * h + e];
+        const bf16x8_t bp = pack8(pv);
+        const int vb = (32 * bi + 16 * h) * HD * 2;
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+            oacc[db] = mfma32(lds_tr_frag(myV + (vb + tr_off[db][0]), myV + (vb + tr_off[db][1])),
+                              bp, oacc[db]);
+    }
+    // the four waves' sums, added in wave order: LDS holds [w][head][d]
+    // (heads < H only) and [w][head] after every wave is done with its tile
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(sV);
+    float* redl = red + 4 * 16 * HD;
+    if (li < H) {
+#pragma unroll
+        for (int db = 0; db < HD / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    red[(w * 16 + li) * HD + 32 * db + 8 * gq + 4 * g + e] = oacc[db][4 * gq + e];
+        if (g == 0) redl[w * 16 + li] = l_run;
+    }
+    __syncthreads();
+    const int64_t slot = (int64_t)b * nch + c;
+    for (int idx = tid; idx < H * HD; idx += 256) {
+        const int j = idx / HD, d = idx - j * HD;
+        const float sum = ((red[(0 * 16 + j) * HD + d] + red[(1 * 16 + j) * HD + d]) +
+                           red[(2 * 16 + j) * HD + d]) + red[(3 * 16 + j) * HD + d];
+        part_o[(slot * H + j) * HD + d] = sum;
+    }
+    if (tid < H) {
+        part_ml[(slot * H + tid) * 2] = 0.f;
+        part_ml[(slot * H + tid) * 2 + 1] =
+            ((redl[tid] + redl[16 + tid]) + redl[32 + tid]) + redl[48 + tid];
+    }
+}
+
 // ------------------------------------------------------------------ backward: dq
 template <int HD, bool FUSE>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
@@ -1044,6 +1182,27 @@ hipError_t launch_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t
 }
 
 }  // namespace
+
+int attn_decode_chunks(int npos) { return (int)ceil_div(npos, kDecKeys); }
+
+hipError_t attn_decode_mfma(const float* q, const bf16_t* kc, const bf16_t* vc, int max_seq,
+                            int npos, int B, int H, int hd, float* part_o, float* part_ml,
+                            hipStream_t s) {
+    if (H < 1 || H > 16 || npos < 1 || npos > max_seq) return hipErrorInvalidValue;
+    const int nch = attn_decode_chunks(npos);
+    const float scale_log2 = kLog2e / sqrtf((float)hd);
+    // q and k are RMS-normalised heads (see the forward launcher's bound)
+    const float m_fixed = sqrtf((float)hd) * kLog2e * 1.0625f;
+    if (hd == 128)
+        hipLaunchKernelGGL(k_attn_decode_mfma<128>, dim3(nch, B), dim3(256), 0, s, q, kc, vc,
+                           max_seq, npos, H, scale_log2, m_fixed, nch, part_o, part_ml);
+    else if (hd == 64)
+        hipLaunchKernelGGL(k_attn_decode_mfma<64>, dim3(nch, B), dim3(256), 0, s, q, kc, vc,
+                           max_seq, npos, H, scale_log2, m_fixed, nch, part_o, part_ml);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
                          int64_t ldkv, bf16_t* o, float* lse, int B, int T, int H, int hd,

@@ -22,11 +22,13 @@
 //     range is also cut into slices (raw sums to scratch, then a kernel that
 //     adds them in slice order and applies the epilogue).
 //   * Attention of the H query heads of a token over its cache is split
-//     over chunks of 128 keys (flash-decoding): each workgroup scores one
-//     chunk for every head (two threads per key, the key row read once for
-//     all H heads), stages the chunk's value rows in LDS, keeps the chunk's
-//     max and sum per head and its weighted value sum; a second kernel
-//     merges the chunks.
+//     over chunks of keys (flash-decoding), and a second kernel merges the
+//     chunks.  bf16 runs the chunks on the matrix cores (attn_mfma.hip, 256
+//     keys per workgroup, the fixed softmax offset of QK-normalised heads);
+//     fp32 uses chunks of 128 keys here: each workgroup scores one chunk for
+//     every head (two threads per key, the key row read once for all H
+//     heads), stages the chunk's value rows in LDS, keeps the chunk's max and
+//     sum per head and its weighted value sum.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -397,11 +399,23 @@ template <typename T>
 hipError_t decode_attn(const float* q, const T* kc, const T* vc, int max_seq, int npos, int B,
                        int H, int hd, float* part_o, float* part_ml, T* o, hipStream_t s) {
     if (H > kMaxHeads || hd > 128 || hd % 16) return hipErrorInvalidValue;
-    const int nch = decode_chunks(npos);
-    hipLaunchKernelGGL(k_decode_attn<T>, dim3(nch, B), dim3(kDecThreads), 0, s, q, kc, vc, max_seq,
-                       npos, H, hd, 1.f / sqrtf((float)hd), nch, part_o, part_ml);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    int nch;
+    if (std::is_same<T, bf16_t>::value && (hd == 64 || hd == 128)) {
+        // matrix-core chunks of 256 keys with the fixed softmax offset (the
+        // step's queries and cached keys are QK-normalised)
+        nch = attn_decode_chunks(npos);
+        const hipError_t e = attn_decode_mfma(reinterpret_cast<const float*>(q),
+                                              reinterpret_cast<const bf16_t*>(kc),
+                                              reinterpret_cast<const bf16_t*>(vc), max_seq, npos,
+                                              B, H, hd, part_o, part_ml, s);
+        if (e != hipSuccess) return e;
+    } else {
+        nch = decode_chunks(npos);
+        hipLaunchKernelGGL(k_decode_attn<T>, dim3(nch, B), dim3(kDecThreads), 0, s, q, kc, vc,
+                           max_seq, npos, H, hd, 1.f / sqrtf((float)hd), nch, part_o, part_ml);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(k_decode_combine<T>, dim3(B, H), dim3(128), 0, s, part_o, part_ml, nch, H,
                        hd, o);
     return hipGetLastError();

@@ -63,6 +63,15 @@ size_t gemm_splitk_bytes(int M, int N, int K);
 // attn_fwd / attn_bwd below run the per-row kernels of attn_simt.hip for
 // float and the matrix-core kernels for bf16.
 // Matrix-core kernels (bf16, T a multiple of 64, hd 64 or 128).
+// Decode attention of one token per sequence over a bf16 cache on the matrix
+// cores (q fp32 [B, H, hd] with RMS-normalised heads; kc, vc [B][max_seq][hd]
+// with RMS-normalised keys; hd 64 or 128, H <= 16): per chunk of
+// attn_decode_chunks(npos) <= decode_chunks(npos) writes part_o [B][chunk][H][hd]
+// and part_ml [B][chunk][H][2] = {0, sum p} for the combine kernel.
+int attn_decode_chunks(int npos);
+hipError_t attn_decode_mfma(const float* q, const bf16_t* kc, const bf16_t* vc, int max_seq,
+                            int npos, int B, int H, int hd, float* part_o, float* part_ml,
+                            hipStream_t s);
 // qk_normed: q and k heads are RMS-normalised (QK-norm), which bounds every
 // score and lets the bf16 forward drop its running maximum
 hipError_t attn_fwd_mfma(const bf16_t* q, const bf16_t* k, const bf16_t* v, int64_t ldq,
