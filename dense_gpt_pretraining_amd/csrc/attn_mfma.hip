@@ -724,13 +724,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     // copy plan: the wave's i-th copy moves tile row (w NI + i) RPI + lane /
     // (HD/8), chunk position lane % (HD/8).  The Q vector of matrix row r sits
     // at (t = r / H, head j = r % H) of the qkv buffer; (t, j) of each copied
-    // row advance incrementally by kQT rows per tile.
+    // row step back incrementally by kQT rows per tile.  The row tiles are
+    // taken from the last one back to the first: every key block of a
+    // sequence ends at the same row, so blocks of one sequence that run
+    // together stream the same Q / dO tile at the same time (the sequence is
+    // the workgroup index modulo B, so with B a multiple of 8 they also share
+    // an XCD and its L2).
     int cp_t[NI], cp_j[NI], cp_c[NI], cp_row[NI];
+    const int r_last = r_begin + max(0, (r_end - r_begin) / kQT - 1) * kQT;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int row = (w * NI + i) * RPI + lane / (HD / 8);
         const int p = lane % (HD / 8);
-        const int rr = r_begin + row;
+        const int rr = r_last + row;
         cp_row[i] = row;
         cp_t[i] = rr / H;
         cp_j[i] = rr - cp_t[i] * H;
@@ -756,9 +762,9 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
             const int doff = cp_row[i] * HD * 2 + cp_c[i];
             lds_copy<16>(rq, qoff, sQ + (w * NI + i) * 1024);
             lds_copy<16>(rd, doff, sD + (w * NI + i) * 1024);
-            cp_j[i] += step_j;
-            cp_t[i] += step_t;
-            if (cp_j[i] >= H) { cp_j[i] -= H; cp_t[i] += 1; }
+            cp_j[i] -= step_j;
+            cp_t[i] -= step_t;
+            if (cp_j[i] < 0) { cp_j[i] += H; cp_t[i] -= 1; }
         }
         // one wave copies the tile's -lse log2 e values, another its -delta
         if (w == 0)
@@ -789,12 +795,12 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
     const int first_vis = key * H;            // first row that sees this lane's key
     const int w_first_vis = wkey0 * H;        // first row that sees the wave's first key
     const int w_all_vis = (wkey0 + 31) * H;   // from here on every row sees every key
-    if (n_qt > 0) issue(r_begin, 0);
+    if (n_qt > 0) issue(r_last, 0);
     for (int it = 0; it < n_qt; ++it) {
-        const int R0 = r_begin + it * kQT;
+        const int R0 = r_last - it * kQT;
         wait_vmem();
         barrier_nofence();
-        if (it + 1 < n_qt) issue(R0 + kQT, (it + 1) & 1);
+        if (it + 1 < n_qt) issue(R0 - kQT, (it + 1) & 1);
         const char* sQ = sm + (it & 1) * BUF;
         const char* sD = sQ + TQ;
         const float* sL = reinterpret_cast<const float*>(sD + TQ);
