@@ -231,6 +231,8 @@ def main():
                     help="also time prefill and KV-cache decode steps (1) or not (0)")
     ap.add_argument("--optimizer", type=int, default=1,
                     help="also time one Muon + AdamW optimizer step (1) or not (0)")
+    ap.add_argument("--cpu-baseline", type=int, default=1,
+                    help="also time the oracle on one sequence of the workload (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
@@ -304,7 +306,7 @@ def main():
     gen = generation_timing(model, params, cfg, tokens) if args.generation else None
     optim = optimizer_timing(model, params, grads, cfg, 5) if args.optimizer else None
 
-    cpu = cpu_baseline(cfg)
+    cpu = cpu_baseline(cfg) if args.cpu_baseline else None
 
     out = {
         "metric": METRIC,
