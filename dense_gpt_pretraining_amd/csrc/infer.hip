@@ -149,6 +149,105 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
     }
 }
 
+// sum over k slices s = 0 .. S-1 of part[(s * B + b) * N + n], added in slice
+// order; the loads of eight slices are issued before their adds
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int S, int B, int N,
+                                           int b, int n) {
+    const float* p = part + (int64_t)b * N + n;
+    const int64_t st = (int64_t)B * N;
+    float v = 0.f;
+    int sl = 0;
+    for (; sl + 8 <= S; sl += 8) {
+        float a[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = p[(sl + u) * st];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v += a[u];
+    }
+    for (; sl < S; ++sl) v += p[sl * st];
+    return v;
+}
+
+// The QKV product's k slices summed in slice order for token row b = blockIdx.x,
+// then its epilogue: u = r[b] * sum; the query heads and the key head are
+// rotated at position pos (pair (i, i + hd/2) by pos * base^(-2i/hd), the
+// angle in fp64 as the step's tables) and RMS-normalised (queries to q_out in
+// fp32, the key into its cache row); the value head goes to its cache row.
+// Thread t takes rotary pairs t, t + 1024, ... of the row's (H + 2) hd/2
+// pairs, head by head, so a head's pairs are hd/2 consecutive lanes.
+__global__ __launch_bounds__(1024) void k_qkv_rope_reduce(
+    const float* __restrict__ part, int S, int B, int H, int hd, const float* __restrict__ rs,
+    int pos, double base, float eps, float* __restrict__ q_out, bf16_t* __restrict__ kc,
+    bf16_t* __restrict__ vc, int max_seq) {
+    const int b = blockIdx.x, t = threadIdx.x, half = hd >> 1;
+    const int N = (H + 2) * hd;
+    const float r = rs[b];
+    const int64_t crow = ((int64_t)b * max_seq + pos) * hd;
+    const int npairs = (H + 2) * half;
+    // every pass covers whole heads (1024 is a multiple of hd/2)
+    for (int p0 = 0; p0 < npairs; p0 += 1024) {
+        const int p = p0 + t;
+        const bool ok = p < npairs;
+        const int h = ok ? p / half : H + 1, i = p % half;
+        float u0 = 0.f, u1 = 0.f;
+        if (ok) {
+            const int n0 = h * hd + i;
+            u0 = r * slice_sum(part, S, B, N, b, n0);
+            u1 = r * slice_sum(part, S, B, N, b, n0 + half);
+        }
+        if (h == H + 1) {   // the value head (uniform over its lanes)
+            if (ok) {
+                vc[crow + i] = f2bf(u0);
+                vc[crow + i + half] = f2bf(u1);
+            }
+            continue;
+        }
+        const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
+        const float c = (float)cos(ang), sn = (float)sin(ang);
+        const float y0 = u0 * c - u1 * sn, y1 = u0 * sn + u1 * c;
+        // the head's sum of squares over its hd/2 lanes
+        float ss = y0 * y0 + y1 * y1;
+        for (int o = half >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+        const float rr = 1.f / sqrtf(ss / (float)hd + eps);
+        if (h < H) {
+            float* qo = q_out + ((int64_t)b * H + h) * hd;
+            qo[i] = y0 * rr;
+            qo[i + half] = y1 * rr;
+        } else {
+            kc[crow + i] = f2bf(y0 * rr);
+            kc[crow + i + half] = f2bf(y1 * rr);
+        }
+    }
+}
+
+// A residual product's k slices summed in slice order for token row
+// b = blockIdx.x, plus the residual aux: y = bf16(aux + sum); and the RMS
+// scale of the stored row, r[b] = 1 / sqrt(mean(y^2) + eps), for the next
+// product's row scale.
+__global__ __launch_bounds__(1024) void k_resid_rms_reduce(
+    const float* __restrict__ part, int S, int B, int N, const bf16_t* __restrict__ aux,
+    bf16_t* __restrict__ y, float eps, float* __restrict__ r_out) {
+    __shared__ float red[16];
+    const int b = blockIdx.x, t = threadIdx.x;
+    float ss = 0.f;
+    for (int n = t; n < N; n += 1024) {
+        const float v = slice_sum(part, S, B, N, b, n);
+        const int64_t o = (int64_t)b * N + n;
+        const bf16_t w = f2bf(bf2f(aux[o]) + v);
+        y[o] = w;
+        const float f = bf2f(w);
+        ss += f * f;
+    }
+    ss = wave_sum(ss);
+    if ((t & 63) == 0) red[t >> 6] = ss;
+    __syncthreads();
+    if (t == 0) {
+        float tot = 0.f;
+        for (int w = 0; w < 16; ++w) tot += red[w];
+        r_out[b] = 1.f / sqrtf(tot / (float)N + eps);
+    }
+}
+
 // Rotary at position pos then QK-norm for the H query heads (fp32 out) and
 // the key head (T, into the cache row); the value head is copied to its cache
 // row.  One wave per (token b, head h); lane i holds the pair (i, i + hd/2).
@@ -382,6 +481,44 @@ hipError_t gemv(int mode, const bf16_t* x, int64_t ldx, int B, const bf16_t* W, 
             return launch_gemv<EPI_RESID>(x, ldx, B, W, N, K, rs, aux, y, ldy, part, S, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+// The fused decode products: S k slices (gemv_splits of the shape) whose raw
+// sums go to `part`, then the row-wise reduce with its epilogue.  Both need
+// S > 1 (the caller checks gemv_fused_ok).
+bool gemv_fused_ok(int N, int K, int B, size_t part_elems) {
+    const int S = gemv_splits(N, K);
+    return B >= 1 && B <= 32 && K % 64 == 0 && S > 1 && (size_t)S * B * N <= part_elems;
+}
+
+hipError_t gemv_qkv_rope(const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int H, int hd,
+                         int K, const float* rs, int pos, double base, float eps, float* q_out,
+                         bf16_t* kc, bf16_t* vc, int max_seq, float* part, hipStream_t s) {
+    const int N = (H + 2) * hd;
+    const int S = gemv_splits(N, K);
+    if (S < 2 || 1024 % (hd / 2)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gemv_mfma<EPI_STORE_F32>, dim3((unsigned)ceil_div(N, kGvRows), S),
+                       dim3(kGvThreads), 0, s, x, ldx, B, W, N, K, rs, nullptr, nullptr, 0, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qkv_rope_reduce, dim3(B), dim3(1024), 0, s, part, S, B, H, hd, rs, pos,
+                       base, eps, q_out, kc, vc, max_seq);
+    return hipGetLastError();
+}
+
+hipError_t gemv_resid_rms(const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
+                          const bf16_t* aux, bf16_t* y, float eps, float* r_out, float* part,
+                          hipStream_t s) {
+    const int S = gemv_splits(N, K);
+    if (S < 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_gemv_mfma<EPI_STORE_F32>, dim3((unsigned)ceil_div(N, kGvRows), S),
+                       dim3(kGvThreads), 0, s, x, ldx, B, W, N, K, nullptr, nullptr, nullptr, 0,
+                       part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_resid_rms_reduce, dim3(B), dim3(1024), 0, s, part, S, B, N, aux, y, eps,
+                       r_out);
+    return hipGetLastError();
 }
 
 template <typename T>

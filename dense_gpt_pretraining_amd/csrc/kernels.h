@@ -172,6 +172,20 @@ hipError_t gemv(int mode, const bf16_t* x, int64_t ldx, int B, const bf16_t* W, 
                 const float* rs, const bf16_t* aux, void* y, int64_t ldy, float* part,
                 size_t part_elems, hipStream_t s);
 int gemv_splits(int N, int K);
+// Decode products whose split-K reduce carries the step's row work: both run
+// gemv_splits(N, K) > 1 slices into part (gemv_fused_ok checks the shape and
+// the scratch).  gemv_qkv_rope: qkv = rs[b] x W^T (N = (H+2) hd), then rotary
+// at position pos (angle pos * base^(-2i/hd) in fp64) and QK-norm; query
+// heads to q_out fp32 [B][H][hd], the key and value heads to cache row pos of
+// kc, vc ([B][max_seq][hd]).  gemv_resid_rms: y = bf16(aux + x W^T) ([B][N],
+// aux and y with row stride N), and r_out[b] = 1/sqrt(mean(y_b^2) + eps).
+bool gemv_fused_ok(int N, int K, int B, size_t part_elems);
+hipError_t gemv_qkv_rope(const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int H, int hd,
+                         int K, const float* rs, int pos, double base, float eps, float* q_out,
+                         bf16_t* kc, bf16_t* vc, int max_seq, float* part, hipStream_t s);
+hipError_t gemv_resid_rms(const bf16_t* x, int64_t ldx, int B, const bf16_t* W, int N, int K,
+                          const bf16_t* aux, bf16_t* y, float eps, float* r_out, float* part,
+                          hipStream_t s);
 // rotary at position pos + QK-norm of B tokens' qkv rows ([B][(H+2) hd], row
 // stride ldq): query heads into q_out fp32 [B][H][hd], the key head and the
 // value head into cache row pos of kc, vc ([B][max_seq][hd])

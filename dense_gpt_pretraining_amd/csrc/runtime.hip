@@ -704,10 +704,43 @@ int decode_step(const nc_config& c, const T* params, const int32_t* tok, int pos
     const int64_t per = (int64_t)B * max_seq * hd;
     float* gp = reinterpret_cast<float*>(ws + d.gpart);
     const size_t gpe = d.gpart_elems;
-    NC_TRY(nc::rope_tables(pos + 1, hd, c.rope_base, cos_t, sin_t, s));
     T* x = P(d.x0);
     T* xn = P(d.x1);
     T* xm = P(d.xm);
+    // bf16: the QKV product's reduce also applies rotary at pos and QK-norm and
+    // fills the cache row, and the two residual products' reduces also emit
+    // the next row scale, so a layer is 10 launches
+    bool fused = false;
+    if constexpr (std::is_same<T, nc::bf16_t>::value)
+        fused = nc::gemv_fused_ok(Wq, D, B, gpe) && nc::gemv_fused_ok(D, H * hd, B, gpe) &&
+                nc::gemv_fused_ok(D, F, B, gpe) && 1024 % (hd / 2) == 0;
+    if (fused) {
+        if constexpr (std::is_same<T, nc::bf16_t>::value) {
+            NC_TRY(nc::embed_fwd<T>(Wt + lay[0].offset, tok, B, D, eps, x, r, s));
+            NC_TRY(nc::rms_stats<T>(x, B, D, eps, r, s));
+            for (int l = 0; l < L; ++l) {
+                T* kc = cache + 2 * l * per;
+                T* vc = cache + (2 * l + 1) * per;
+                NC_TRY(nc::gemv_qkv_rope(x, D, B, Wl(l, 0), H, hd, D, r, pos,
+                                         (double)c.rope_base, eps, q, kc, vc, max_seq, gp, s));
+                NC_TRY(nc::decode_attn<T>(q, kc, vc, max_seq, pos + 1, B, H, hd,
+                                          reinterpret_cast<float*>(ws + d.part_o),
+                                          reinterpret_cast<float*>(ws + d.part_ml), P(d.o), s));
+                NC_TRY(nc::gemv_resid_rms(P(d.o), H * hd, B, Wl(l, 3), D, H * hd, x, xm, eps, r,
+                                          gp, s));
+                NC_TRY(dec_gemm<T>(nc::EPI_ROWSCALE_RELU2, xm, D, B, Wl(l, 4), F, D, r, nullptr,
+                                   P(d.g), F, s, gp, gpe));
+                NC_TRY(nc::gemv_resid_rms(P(d.g), F, B, Wl(l, 5), D, F, xm, xn, eps, r, gp, s));
+                std::swap(x, xn);
+            }
+            // r is the final norm's scale of x
+            NC_TRY(dec_gemm<T>(nc::EPI_STORE_F32, x, D, B, Wt + lay[1 + 6 * L].offset, V, D, r,
+                               nullptr, logits, V, s));
+            NC_TRY(nc::softcap_rows(logits, (int64_t)B * V, c.softcap, s));
+            return NC_OK;
+        }
+    }
+    NC_TRY(nc::rope_tables(pos + 1, hd, c.rope_base, cos_t, sin_t, s));
     NC_TRY(nc::embed_fwd<T>(Wt + lay[0].offset, tok, B, D, eps, x, r, s));
     for (int l = 0; l < L; ++l) {
         T* kc = cache + 2 * l * per;
