@@ -232,3 +232,51 @@ def _muon_bf16_rounded(theta, g):
     rows, cols = theta.shape
     lr = OCFG["muon_lr"]
     return theta * (1 - lr * OCFG["muon_weight_decay"]) - lr * np.sqrt(max(1.0, rows / cols)) * X
+
+
+def _curves():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "training_curves.json")
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("run", [0, 1])
+def test_training_loop_follows_the_oracle_curve(run):
+    """The step and the optimizer chained as a training loop on one fixed
+    batch: forward+backward, then Muon + AdamW with clipping and a warm-up +
+    cosine schedule, repeated.  The loss before every step is compared with
+    the float64 oracle's run of the same loop (tests/golden/training_curves.json,
+    written by make_training_curves.py from oracle/ alone): fp32 within
+    1e-3 + 1e-2 of the oracle's value, bf16 (whose parameters are rounded to
+    bf16 after every step) within 1e-2 + 1e-1 of it; the loss falls from
+    ln V to a few percent of it."""
+    from dense_gpt_pretraining_amd import Model, Optimizer
+    from dense_gpt_pretraining_amd import binding as b
+    torch = require_gpu()
+    cur = _curves()
+    r = cur["runs"][run]
+    cfg = get_config(r["config"], **r["over"])
+    steps, want = r["steps"], r["losses"]
+    m = Model(cfg)
+    p = m.pack(make_params(cfg))
+    tokens, targets = make_tokens(cfg)
+    opt = Optimizer(m, cur["optimizer"])
+    opt.init(p)
+    g = torch.empty(m.n_params, dtype=torch.float32, device="cuda")
+    got = []
+    for t in range(1, steps + 1):
+        loss, _ = m.forward_backward(p, tokens, targets, grads=g)
+        got.append(float(loss.item()))
+        opt.step(p, g, t, b.nc_lr_multiplier(t - 1, steps, cur["warmup"], cur["final_frac"]))
+    torch.cuda.synchronize()
+    print(f"[{r['config']}] loss every 5 steps, GPU / oracle: " +
+          ", ".join(f"{a:.4f}/{w:.4f}" for a, w in zip(got[::5], want[::5])) +
+          f", last {got[-1]:.4f}/{want[-1]:.4f}")
+    fp32 = cfg["dtype"] == "f32"
+    ra, rr = (1e-3, 1e-2) if fp32 else (1e-2, 1e-1)
+    for t, (a, w) in enumerate(zip(got, want)):
+        assert np.isfinite(a) and abs(a - w) <= ra + rr * abs(w), (t, a, w)
+    assert got[-1] < 0.05 * got[0]

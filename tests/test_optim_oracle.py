@@ -237,3 +237,32 @@ def _adam_l2(theta, g, m, v, t, lr, b1, b2, eps, wd):
     m = b1 * m + (1 - b1) * g
     v = b2 * v + (1 - b2) * g * g
     return theta - lr * (m / (1 - b1 ** t)) / (np.sqrt(v / (1 - b2 ** t)) + eps), m, v
+
+
+def test_stored_training_curves_are_the_oracle_s():
+    """tests/golden/training_curves.json (the GPU training-loop test's
+    reference) holds what the oracle computes: the tiny run is recomputed
+    here in full; both runs start at the loss of an all-but-zero unembedding
+    (std 0.001), within 1e-2 of ln V, and fall to a few percent of it."""
+    import json
+    import math
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(here, "golden", "training_curves.json")) as f:
+        cur = json.load(f)
+    for r in cur["runs"]:
+        V = get_config(r["config"], **r["over"])["vocab"]
+        assert abs(r["losses"][0] - math.log(V)) < 1e-2
+        assert r["losses"][-1] < 0.05 * r["losses"][0]
+    r = cur["runs"][0]
+    assert r["config"] == "tiny"
+    cfg = get_config("tiny")
+    params = make_params(cfg)
+    tokens, targets = make_tokens(cfg)
+    st = oo.init_state(params)
+    for t in range(1, r["steps"] + 1):
+        loss, grads = oracle.forward_backward(cfg, {k: st["master"][k] for k in params}, tokens,
+                                              targets)
+        assert loss == pytest.approx(r["losses"][t - 1], rel=1e-12, abs=1e-12)
+        oo.step(cur["optimizer"], st, grads, t,
+                oo.lr_multiplier(t - 1, r["steps"], cur["warmup"], cur["final_frac"]))
