@@ -424,6 +424,61 @@ __device__ __forceinline__ void qkv_rope_pass128(const EpiDev& e, bf16_t* C, int
     const int head = ncol0 >> 7;
     const bool rot = head <= H;
     const int l16 = lane & 15, rsub = lane >> 4;
+    // Whole 32-row passes inside one sequence (every pass of the step's
+    // shapes: rows are tokens, sequences are multiples of 32 long) take a
+    // branch-free path: the position is the pass's first position plus the
+    // row, and the stores are buffer stores at scalar row offsets.
+    if (mrow0 + 32 <= M && (e.seq_len & 31) == 0 && ldc <= (1 << 24)) {
+        const int pos0 = mrow0 % e.seq_len;
+        const buf_rsrc_t rc = make_rsrc(C + (int64_t)mrow0 * ldc + ncol0);
+        const int voff = (rsub * (int)ldc + 4 * l16) * 2;
+        float4 c4[8], s4[8];
+        if (rot) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int pos = pos0 + 4 * t + rsub;
+                c4[t] = *reinterpret_cast<const float4*>(e.cos_t + pos * 64 + 4 * l16);
+                s4[t] = *reinterpret_cast<const float4*>(e.sin_t + pos * 64 + 4 * l16);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 4 * t + rsub;
+            const float4 a = *reinterpret_cast<const float4*>(stage + row * 128 + ((l16 ^ row) << 2));
+            const float4 b =
+                *reinterpret_cast<const float4*>(stage + row * 128 + (((16 + l16) ^ row) << 2));
+            const float rs = rsl[row];
+            float x1[4] = {a.x * rs, a.y * rs, a.z * rs, a.w * rs};
+            float x2[4] = {b.x * rs, b.y * rs, b.z * rs, b.w * rs};
+            if (rot) {
+                const float cs[4] = {c4[t].x, c4[t].y, c4[t].z, c4[t].w};
+                const float sn[4] = {s4[t].x, s4[t].y, s4[t].z, s4[t].w};
+                float ss = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float y1 = x1[q] * cs[q] - x2[q] * sn[q];
+                    const float y2 = x1[q] * sn[q] + x2[q] * cs[q];
+                    x1[q] = y1;
+                    x2[q] = y2;
+                    ss += y1 * y1 + y2 * y2;
+                }
+                ss = row16_sum(ss);
+                const float rr = __builtin_amdgcn_rsqf(ss * (1.f / 128.f) + e.eps);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    x1[q] *= rr;
+                    x2[q] *= rr;
+                }
+                if (l16 == 0) e.rqk[(int64_t)(mrow0 + row) * (H + 1) + head] = rr;
+            }
+            const int so = 4 * t * (int)ldc * 2;
+            const u32x2_t w1 = {pack_bf2(x1[0], x1[1]), pack_bf2(x1[2], x1[3])};
+            const u32x2_t w2 = {pack_bf2(x2[0], x2[1]), pack_bf2(x2[2], x2[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(w1, rc, voff, so, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(w2, rc, voff + 128, so, kNonTemporal);
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         const int row = 4 * t + rsub;
