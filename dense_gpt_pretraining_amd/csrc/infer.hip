@@ -179,7 +179,15 @@ __global__ __launch_bounds__(1024) void k_qkv_rope_reduce(
     const float* __restrict__ part, int S, int B, int H, int hd, const float* __restrict__ rs,
     int pos, double base, float eps, float* __restrict__ q_out, bf16_t* __restrict__ kc,
     bf16_t* __restrict__ vc, int max_seq) {
+    // the hd/2 angles of position pos, once per workgroup
+    __shared__ float cs_l[64], sn_l[64];
     const int b = blockIdx.x, t = threadIdx.x, half = hd >> 1;
+    if (t < half) {
+        const double ang = (double)pos * pow(base, -2.0 * (double)t / (double)hd);
+        cs_l[t] = (float)cos(ang);
+        sn_l[t] = (float)sin(ang);
+    }
+    __syncthreads();
     const int N = (H + 2) * hd;
     const float r = rs[b];
     const int64_t crow = ((int64_t)b * max_seq + pos) * hd;
@@ -202,8 +210,7 @@ __global__ __launch_bounds__(1024) void k_qkv_rope_reduce(
             }
             continue;
         }
-        const double ang = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
-        const float c = (float)cos(ang), sn = (float)sin(ang);
+        const float c = cs_l[i], sn = sn_l[i];
         const float y0 = u0 * c - u1 * sn, y1 = u0 * sn + u1 * c;
         // the head's sum of squares over its hd/2 lanes
         float ss = y0 * y0 + y1 * y1;
