@@ -148,3 +148,31 @@ def test_causality_on_gpu():
     a, b = tl0.cpu().numpy(), tl1.cpu().numpy()
     np.testing.assert_array_equal(a[0, :t0], b[0, :t0])
     assert np.any(a[0, t0:] != b[0, t0:])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("over", [
+    # one query head (MQA degenerates to single-head attention), the shortest
+    # sequence the bf16 kernels take, a vocabulary off the 256-column padding
+    dict(n_layer=1, d_model=64, n_head=1, head_dim=64, d_mlp=256, vocab=300, seq_len=64,
+         batch=1),
+    # heads whose QKV width (H + 2) hd = 576 is no multiple of the 256-wide tile, d_model
+    # != H hd, odd batch, vocabulary just past a padding multiple
+    dict(n_layer=2, d_model=192, n_head=7, head_dim=64, d_mlp=320, vocab=513, seq_len=128,
+         batch=3),
+])
+def test_degenerate_and_ragged_shapes(dtype, over):
+    """Shapes the method allows but the named configurations never reach:
+    a single query head, d_model different from H hd, ragged GEMM tiles in
+    every product and a padded vocabulary, at fp32 and bf16, against the
+    oracle with the unembedding at std 0.05 so the blocks' gradients matter."""
+    cfg = get_config("tiny", dtype=dtype, **over)
+    params = make_params(cfg)
+    w = np.random.default_rng(11).standard_normal(params["wlm"].shape).astype(np.float32) * 0.05
+    if dtype == "bf16":
+        from nc_synth import bf16_round
+        w = bf16_round(w)
+    params["wlm"] = w
+    tokens, targets = make_tokens(cfg)
+    tol = (1e-4, 1e-4, 0.9999) if dtype == "f32" else (1e-2, 3e-2, 0.999)
+    _compare(cfg, params, tokens, targets, *tol, f"{dtype} {over['n_head']}x{over['head_dim']}")
