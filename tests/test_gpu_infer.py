@@ -100,3 +100,33 @@ def test_generation_at_the_d20_workload_shape():
     errs = [_check(g, w, False, f"decode {1984 + i}") for i, (g, w) in enumerate(zip(got, want))]
     print(f"[d20 generation] 64 decoded positions: worst logits rel-L2 "
           f"{max(e for e, _ in errs):.2e}, lowest cosine {min(c for _, c in errs):.6f}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_generation_on_small_ragged_shapes(dtype):
+    """Prefill then decode on shapes whose products are too small to split
+    over k, so bf16 decode takes its unfused path (separate rotary / QK-norm
+    and RMS kernels; the named configurations all take the fused one), with
+    one query head and a padded vocabulary; and a seven-head model with
+    d_model != H hd."""
+    from dense_gpt_pretraining_amd import Generator
+    require_gpu()
+    for over in (dict(n_layer=1, d_model=64, n_head=1, head_dim=64, d_mlp=256, vocab=300,
+                      batch=2),
+                 dict(n_layer=2, d_model=192, n_head=7, head_dim=64, d_mlp=320, vocab=513,
+                      batch=3)):
+        from dense_gpt_pretraining_amd import Model
+        cfg = get_config("tiny", dtype=dtype, seq_len=64, **over)
+        cfg96 = get_config("tiny", dtype=dtype, seq_len=96, **over)
+        params = make_params(cfg)
+        w = np.random.default_rng(9).standard_normal(params["wlm"].shape).astype(np.float32)
+        params["wlm"] = bf16_round(w * 0.05) if dtype == "bf16" else w * 0.05
+        tokens = make_tokens(cfg96, batch=cfg["batch"])[0]
+        m = Model(cfg)
+        p = m.pack(params)
+        want = oracle.forward_logits(cfg96, params, tokens, positions=list(range(63, 96)))
+        gen = Generator(m, max_seq=100, max_prefill=64)
+        _check(from_dev(gen.prefill(p, tokens[:, :64])), want[:, 0], dtype == "f32", "prefill")
+        for pos in range(64, 96):
+            got = from_dev(gen.decode(p, tokens[:, pos], pos))
+            _check(got, want[:, pos - 63], dtype == "f32", f"decode {pos}")
