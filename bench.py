@@ -235,7 +235,7 @@ def main():
                     help="also time the oracle on one sequence of the workload (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): this build has no "
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 

@@ -1092,7 +1092,7 @@ const char* nc_status_string(int status) {
         case NC_ERR_WORKSPACE: return "workspace smaller than nc_workspace_size";
         case NC_ERR_ALIGN: return "a device pointer is not aligned";
         case NC_ERR_HIP: return "a HIP call or kernel launch failed";
-        case NC_ERR_UNSUPPORTED: return "valid model, but a shape this build does not run";
+        case NC_ERR_UNSUPPORTED: return "valid model, but a shape the library does not run";
         case NC_ERR_CAPACITY: return "output array too small";
         default: return "unknown status";
     }

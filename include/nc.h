@@ -52,7 +52,7 @@ enum {
     NC_ERR_WORKSPACE = -4,   /* workspace smaller than nc_workspace_size */
     NC_ERR_ALIGN = -5,       /* a device pointer is not 256-byte aligned */
     NC_ERR_HIP = -6,         /* a HIP call or kernel launch failed */
-    NC_ERR_UNSUPPORTED = -7, /* valid model, but a shape this build does not run */
+    NC_ERR_UNSUPPORTED = -7, /* valid model, but a shape the library does not run */
     NC_ERR_CAPACITY = -8     /* output array too small (nc_param_layout) */
 };
 
