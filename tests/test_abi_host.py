@@ -192,6 +192,11 @@ def test_ops_validation():
             b.nc_op_softcap_ce(dtype, 4, 100, cap + 8, 0x1000, 0x2000, 15.0, 0x3000, 0.25,
                                0x4000, 1, None)
         assert ei.value.code == -7
+    # the attention flag does not relax the shape checks
+    with pytest.raises(b.NcError) as ei:
+        b.nc_op_attention_fwd(1, 1, 48, 2, 64, 0x1000, 0x2000, 0x3000, 128, 64, 0x4000, 0x5000,
+                              None, qk_normed=1)
+    assert ei.value.code == -7
     for dtype, vocab in (("bf16", 131072), ("f32", 65536)):
         c = b.make_config({**get_config("tiny"), "dtype": dtype, "vocab": vocab})
         assert b.nc_param_count(c) > 0
@@ -199,6 +204,46 @@ def test_ops_validation():
         with pytest.raises(b.NcError) as ei:
             b.nc_param_count(c)
         assert ei.value.code == -7
+
+
+def test_matmul_epilogue_validation_before_device_work():
+    """Every argument check of the fused-epilogue product fails before a launch,
+    so none of these fake addresses is ever dereferenced."""
+    b = _b()
+    A, B, C, RS, AUX = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+
+    def call(**kw):
+        a = dict(dtype=1, M=8, N=8, K=64, A=A, lda=64, a_kmajor=1, B=B, ldb=64, b_kmajor=1,
+                 Cp=C, ldc=8, mode=5, rowscale=None, aux=None, stream=None)
+        a.update(kw)
+        with pytest.raises(b.NcError) as ei:
+            b.nc_op_matmul_epilogue(**a)
+        return ei.value.code
+
+    assert call(dtype=7) == -3
+    assert call(M=0) == -2 and call(N=0) == -2 and call(K=0) == -2
+    assert call(mode=0) == -2 and call(mode=6) == -2
+    # the row-scaled modes need rowscale, the residual and relu^2 backward need aux
+    for mode in (1, 2, 4):
+        assert call(mode=mode, aux=AUX) == -1
+    for mode in (3, 4):
+        assert call(mode=mode, rowscale=RS) == -1
+    assert call(A=None) == -1 and call(B=None) == -1 and call(Cp=None) == -1
+    assert call(A=A + 8) == -5 and call(Cp=C + 4) == -5
+    assert call(mode=3, aux=AUX + 8) == -5
+    # leading dimensions shorter than the rows they hold
+    assert call(ldc=4) == -2
+    assert call(lda=32) == -2 and call(a_kmajor=0, lda=4) == -2
+    assert call(ldb=32) == -2 and call(b_kmajor=0, ldb=4) == -2
+    # bf16: an mn-major A is not built; an mn-major B only with the
+    # data-gradient modes; K a multiple of 64
+    assert call(a_kmajor=0, lda=8) == -7
+    for mode in (1, 2, 3):
+        assert call(mode=mode, b_kmajor=0, ldb=8, rowscale=RS, aux=AUX) == -7
+    assert call(K=96, lda=96, ldb=96) == -7
+    assert call(lda=68) == -7
+    # fp32 runs every operand-major pair, so only the generic checks apply
+    assert call(dtype=0, A=None, a_kmajor=0, lda=8) == -1
 
 
 OCFG = dict(adam_lr=3e-3, adam_beta1=0.8, adam_beta2=0.95, adam_eps=1e-10,
