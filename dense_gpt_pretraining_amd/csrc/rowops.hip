@@ -206,6 +206,18 @@ __device__ __forceinline__ void unpack_chunk<bf16_t>(const uint4& raw, float* ou
     out[0] = bf_lo(raw.x); out[1] = bf_hi(raw.x); out[2] = bf_lo(raw.y); out[3] = bf_hi(raw.y);
     out[4] = bf_lo(raw.z); out[5] = bf_hi(raw.z); out[6] = bf_lo(raw.w); out[7] = bf_hi(raw.w);
 }
+template <typename T>
+__device__ __forceinline__ uint4 pack_chunk(const float* in);
+template <>
+__device__ __forceinline__ uint4 pack_chunk<float>(const float* in) {
+    return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]),
+                      __float_as_uint(in[3]));
+}
+template <>
+__device__ __forceinline__ uint4 pack_chunk<bf16_t>(const float* in) {
+    return make_uint4(pack_bf2(in[0], in[1]), pack_bf2(in[2], in[3]), pack_bf2(in[4], in[5]),
+                      pack_bf2(in[6], in[7]));
+}
 
 // tanh(y) = 1 - 2 / (exp(2y) + 1) on the hardware exp2 and reciprocal units;
 // saturates to +-1 (exp2 overflow gives 1/inf = 0).  Takes y2 = 2 y log2 e
@@ -290,6 +302,12 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     const float zk = kTwoLog2e / cap;
     // exp(c) = 2^(s log2e (1 - 2r)) = 2^(a + b r)
     const float a = cap * kL2e, bb = -2.f * cap * kL2e;
+    // With t = c/s = 1 - 2r, dL/dz = (softmax(c) - onehot) (1 - t^2) and
+    // 1 - t^2 = 4 r (1 - r), so the softmax part of a column's gradient is
+    // sc (4 / sum_j e_j) * e r (1 - r): every factor but the row's constant is
+    // known in the first pass.  That pass overwrites each raw logit in
+    // registers with g = e r (1 - r) in the storage type (zero for padding
+    // columns), and the gradient pass is one product per column.
     uint4 raw[MAXC];
     float ssum = 0.f;
 #pragma unroll
@@ -297,17 +315,29 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
         const int64_t c = ((int64_t)ci * kCeThreads + threadIdx.x) * VEC;
         if (c < ldz) {
             raw[ci] = *reinterpret_cast<const uint4*>(zr + c);
-            float v[VEC];
+            float v[VEC], g[VEC];
             unpack_chunk<T>(raw[ci], v);
             if (c + VEC <= V) {
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * zk), a));
+                for (int k = 0; k < VEC; ++k) {
+                    const float r = tanh_r(v[k] * zk);
+                    const float e = __builtin_amdgcn_exp2f(fmaf(bb, r, a));
+                    ssum += e;
+                    g[k] = e * fmaf(-r, r, r);
+                }
             } else {
 #pragma unroll
-                for (int k = 0; k < VEC; ++k)
-                    if (c + k < V) ssum += __builtin_amdgcn_exp2f(fmaf(bb, tanh_r(v[k] * zk), a));
+                for (int k = 0; k < VEC; ++k) {
+                    g[k] = 0.f;
+                    if (c + k < V) {
+                        const float r = tanh_r(v[k] * zk);
+                        const float e = __builtin_amdgcn_exp2f(fmaf(bb, r, a));
+                        ssum += e;
+                        g[k] = e * fmaf(-r, r, r);
+                    }
+                }
             }
+            raw[ci] = pack_chunk<T>(g);
         }
     }
     ssum = block_sum(ssum, red);
@@ -323,41 +353,27 @@ __global__ __launch_bounds__(kCeThreads) void k_softcap_ce(
     // every thread has finished reading z[y] before any thread overwrites it
     __syncthreads();
     const float sc = rowscale[row] * inv_n;
-    // sc exp(c - lse) = 2^(a2 + b r): the row scale (positive) joins the
-    // exponent
-    const float a2 = a - lse * kL2e + __log2f(sc);
-    // dL/dz = (softmax(c) - onehot) (1 - (c/s)^2) = (p - onehot) (1 - t^2);
-    // this is its softmax part, sc p (1 - t^2)
-    auto grad = [&](float x) {
-        const float r = tanh_r(x * zk);
-        const float t = fmaf(-2.f, r, 1.f);
-        const float p = __builtin_amdgcn_exp2f(fmaf(bb, r, a2));   // sc softmax(c)
-        return p * fmaf(-t, t, 1.f);
-    };
+    const float kr = 4.f * sc / ssum;
     // column indices fit in 32 bits: rows are at most 32 chunks per thread
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int c = (ci * kCeThreads + (int)threadIdx.x) * VEC;
         if (c < ldz) {
-            float v[VEC], o[VEC];
-            unpack_chunk<T>(raw[ci], v);
-            if (c + VEC <= V) {
+            float g[VEC];
+            unpack_chunk<T>(raw[ci], g);
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) o[k] = grad(v[k]);
-            } else {
-                // the row's last valid chunk, and the padding columns (zero)
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) o[k] = c + k < V ? grad(v[k]) : 0.f;
-            }
-            st_vec<T>(zr + c, o);
+            for (int k = 0; k < VEC; ++k) g[k] *= kr;
+            st_vec<T>(zr + c, g);
         }
     }
-    // the target column also carries the onehot term: thread 0 rewrites it
-    // once every chunk store of the row has completed
+    // the target column also carries the onehot term: thread 0 rewrites it,
+    // from its raw logit in fp32, once every chunk store of the row has
+    // completed
     __syncthreads();
     if (threadIdx.x == 0 && y >= 0 && y < V) {   // ids out of range write nothing
-        const float t = fmaf(-2.f, tanh_r(zy * zk), 1.f);
-        Elt<T>::st(zr + y, grad(zy) - sc * fmaf(-t, t, 1.f));
+        const float ry = tanh_r(zy * zk);
+        const float ey = __builtin_amdgcn_exp2f(fmaf(bb, ry, a));
+        Elt<T>::st(zr + y, 4.f * sc * fmaf(-ry, ry, ry) * (ey / ssum - 1.f));
     }
 }
 
