@@ -92,6 +92,20 @@ __device__ __forceinline__ f32x16_t zero16() {
 // 2^x on the hardware exponential unit (no range reduction; -inf -> 0)
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pins the order of a block of STEPS k steps, each R LDS fragment reads and M
+// matrix products: the reads of the first AHEAD steps, then per step M
+// products and the reads of the step AHEAD further on, then the last products
+template <int STEPS, int AHEAD, int R, int M>
+__device__ __forceinline__ void sched_reads_ahead() {
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);
+#pragma unroll
+    for (int i = 0; i < STEPS - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD * M, 0);
+}
+
 // wait for this wave's outstanding global loads (direct LDS copies included)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // barrier without the memory fence of __syncthreads (which would also wait
@@ -225,6 +239,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_mfma(
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
                 s[bi] = mfma32(lds_b128(sK + (bi * 32 * HD * 2 + row_off[kk])), qf[kk], s[bi]);
+        // K fragments are read three k steps ahead of their products (left to
+        // itself the compiler reads each just before its use and waits)
+        sched_reads_ahead<HD / 16, 3, 2, 2>();
         // keys beyond a row's position exist only on tiles that reach past
         // the wave's first position
         if (kb + kKT - 1 > tw_min) {
@@ -537,11 +554,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
         for (int bi = 0; bi < 2; ++bi) {
             f32x16_t s = zero16(), dp = ndl;
             const int rb0 = bi * 32 * HD * 2;
+            // the K and V fragment reads of S and dP run three k steps ahead of
+            // their products; the fence keeps the previous block's transpose
+            // reads out of that schedule
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
                 s = mfma32(lds_b128(sK + (rb0 + row_off[kk])), qf[kk], s);
                 dp = mfma32(lds_b128(sV + (rb0 + row_off[kk])), df[kk], dp);
             }
+            sched_reads_ahead<HD / 16, 3, 2, 2>();
             // keys past the row's position get the score -inf (p = 2^-inf = 0),
             // in a loop of its own so that tiles off the diagonal branch past it
             if (diag) {
