@@ -2,7 +2,7 @@
 """Throughput of one forward+backward pretraining step of the depth-20
 nanochat-style decoder on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20] [--batch B]
 
 A step is nc_forward_backward over one batch of synthetic tokens (Zipf(1.1)
 ids, seeded) with parameters drawn on the device by nc_init_params; all
@@ -233,6 +233,9 @@ def main():
                     help="also time one Muon + AdamW optimizer step (1) or not (0)")
     ap.add_argument("--cpu-baseline", type=int, default=1,
                     help="also time the oracle on one sequence of the workload (1) or not (0)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences per step instead of the configuration's (0: keep it); e.g. "
+                         "4 for one GPU's share of d20's 32 sequences over 8 GPUs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the library has no "
@@ -246,7 +249,7 @@ def main():
     from nc_synth import get_config, make_tokens
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = get_config(args.config)
+    cfg = get_config(args.config, **({"batch": args.batch} if args.batch > 0 else {}))
     model = Model(cfg)
     params = model.init_params(cfg["seed_params"])
     tokens, targets = make_tokens(cfg)
@@ -288,7 +291,8 @@ def main():
     else:
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         achieved = dom["bytes"] / (dom["ms"] / 1e3) / 1e9
-    traffic = measured_traffic(args.config, dom_name)
+    # the counters were read at the configuration's own batch
+    traffic = measured_traffic(args.config, dom_name) if args.batch <= 0 else None
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": round(dom["bytes"] / max(dom["launches"], 1)),
