@@ -3,6 +3,7 @@
 nanochat-style decoder on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config d20] [--batch B]
+                    [--gemm-comparison 0|1]
 
 A step is nc_forward_backward over one batch of synthetic tokens (Zipf(1.1)
 ids, seeded) with parameters drawn on the device by nc_init_params; all
@@ -220,6 +221,79 @@ def cpu_baseline(cfg):
                       f"NumPy fwd+bwd, {dt:.1f} s"}
 
 
+def gemm_comparison(cfg):
+    """The step's plain GEMM shapes timed twice on the same device: the
+    library's kernel through its unit entry points (bf16 output for the
+    forward and data-gradient layouts, fp32 with its k-split for the weight
+    gradients, as in the step) and torch.mm (the vendor BLAS) on contiguous
+    row-major operands.  A reference point for the kernels' rates, not part
+    of the metric."""
+    import torch
+
+    from dense_gpt_pretraining_amd import binding as b
+    D, hd, H, F, V = (cfg[k] for k in ("d_model", "head_dim", "n_head", "d_mlp", "vocab"))
+    N_tok = cfg["batch"] * cfg["seq_len"]
+    Wq = (H + 2) * hd
+    # (name, M, N, K, layout): "fwd" = X W^T, "dgrad" = dY W, "wgrad" = dY^T X
+    shapes = [("fc forward", N_tok, F, D, "fwd"), ("qkv forward", N_tok, Wq, D, "fwd"),
+              ("proj forward", N_tok, D, F, "fwd"), ("unembedding forward", N_tok, V, D, "fwd"),
+              ("fc data gradient", N_tok, D, F, "dgrad"),
+              ("fc weight gradient", F, D, N_tok, "wgrad"), ("qkv weight gradient", Wq, D, N_tok, "wgrad")]
+    stream = torch.cuda.current_stream().cuda_stream
+    out = []
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for name, M, N, K, lay in shapes:
+        reps = 3 if 2.0 * M * N * K > 5e12 else 10
+        g = torch.Generator(device="cuda").manual_seed(1)
+        if lay == "fwd":       # A = X [M, K], B = W [N, K], both k-major
+            A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+            Bm = torch.randn(N, K, device="cuda", generator=g).to(torch.bfloat16)
+            C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            ours = lambda: b.nc_op_matmul_epilogue(1, M, N, K, A.data_ptr(), K, 1, Bm.data_ptr(),
+                                                   K, 1, C.data_ptr(), N, 5, None, None, stream)
+        elif lay == "dgrad":   # A = dY [M, K] k-major, B = W [K, N] mn-major
+            A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+            Bm = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+            C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            ours = lambda: b.nc_op_matmul_epilogue(1, M, N, K, A.data_ptr(), K, 1, Bm.data_ptr(),
+                                                   N, 0, C.data_ptr(), N, 5, None, None, stream)
+        else:                  # A = dY [K, M], B = X [K, N], both mn-major; fp32 out
+            A = torch.randn(K, M, device="cuda", generator=g).to(torch.bfloat16)
+            Bm = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+            C = torch.empty(M, N, device="cuda", dtype=torch.float32)
+            ws = torch.empty(32 * M * N, device="cuda", dtype=torch.float32)
+            ours = lambda: b.nc_op_matmul(1, M, N, K, A.data_ptr(), M, 0, Bm.data_ptr(), N, 0,
+                                          C.data_ptr(), N, ws.data_ptr(), ws.numel() * 4, stream)
+        t_ours = timed(ours, reps)
+        del A, Bm, C
+        torch.cuda.empty_cache()
+        # the vendor BLAS on contiguous row-major operands: [M, K] @ [K, N]
+        X = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        Y = torch.randn(K, N, device="cuda", generator=g).to(torch.bfloat16)
+        Z = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        t_mm = timed(lambda: torch.mm(X, Y, out=Z), reps)
+        del X, Y, Z
+        torch.cuda.empty_cache()
+        fl = 2.0 * M * N * K
+        out.append({"shape": name, "M": M, "N": N, "K": K,
+                    "library_ms": round(t_ours, 4), "library_tflops": round(fl / t_ours / 1e9, 1),
+                    "torch_mm_ms": round(t_mm, 4), "torch_mm_tflops": round(fl / t_mm / 1e9, 1)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +307,9 @@ def main():
                     help="also time one Muon + AdamW optimizer step (1) or not (0)")
     ap.add_argument("--cpu-baseline", type=int, default=1,
                     help="also time the oracle on one sequence of the workload (1) or not (0)")
+    ap.add_argument("--gemm-comparison", type=int, default=0,
+                    help="also time the step's GEMM shapes with the library's kernels and with "
+                         "torch.mm (1) or not (0)")
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences per step instead of the configuration's (0: keep it); e.g. "
                          "4 for one GPU's share of d20's 32 sequences over 8 GPUs")
@@ -311,6 +388,7 @@ def main():
     optim = optimizer_timing(model, params, grads, cfg, 5) if args.optimizer else None
 
     cpu = cpu_baseline(cfg) if args.cpu_baseline else None
+    gemms = gemm_comparison(cfg) if args.gemm_comparison and cfg["dtype"] == "bf16" else None
 
     out = {
         "metric": METRIC,
@@ -339,6 +417,8 @@ def main():
         "generation": gen,
         "kernels": kernels,
     }
+    if gemms is not None:
+        out["gemm_comparison"] = gemms
     print(json.dumps(out))
 
 
