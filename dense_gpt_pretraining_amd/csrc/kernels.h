@@ -135,13 +135,14 @@ hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk,
                            const float* dv, const float* rqk, const float* r1,
                            int N, int Tn, int H, int hd, const float* cos_t,
                            const float* sin_t, T* dqkv, hipStream_t s);
-// dres += dn - r^2 * x * mean(dn * x) over each row; dres_t = (T)dres
+// dres = (has_res ? dres : 0) + dn - r^2 * x * mean(dn * x) over each row,
+// in place, rounded to T (dn holds the row scale's product r * dL/dn)
 template <typename T>
-hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N,
-                          int D, float* dres, T* dres_t, hipStream_t s);
+hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D, T* dres,
+                          bool has_res, hipStream_t s);
 // de[t] = r0[t]*dh[t] - r0[t]^3 * e[t] * mean(dh[t]*e[t]), e[t] = wte[tok[t]]
 template <typename T>
-hipError_t embed_bwd_rows(const float* dh, const T* wte, const int32_t* tok,
+hipError_t embed_bwd_rows(const T* dh, const T* wte, const int32_t* tok,
                           const float* r0, int N, int D, float* de, hipStream_t s);
 // Softcap + cross-entropy over rows of z [N, ldz] (V valid columns).
 // tok_loss[t] = logsumexp(c) - c[y]; if want_grad, z is overwritten by

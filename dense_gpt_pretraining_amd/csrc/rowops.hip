@@ -157,31 +157,33 @@ __global__ __launch_bounds__(kRowThreads) void k_rope_qknorm_bwd(
 
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_embed_bwd_rows(
-    const float* __restrict__ dh, const T* __restrict__ wte,
+    const T* __restrict__ dh, const T* __restrict__ wte,
     const int32_t* __restrict__ tok, const float* __restrict__ r0, int N, int D,
     float* __restrict__ de) {
     constexpr int V = Elt<T>::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= N) return;
-    const float* g = dh + row * D;
+    const T* g = dh + row * D;
     const T* e = wte + (int64_t)tok[row] * D;
     float dot = 0.f;
     for (int c = lane * V; c < D; c += kWave * V) {
-        float ev[V];
+        float ev[V], gv[V];
         ld_vec<T>(e + c, ev);
+        ld_vec<T>(g + c, gv);
 #pragma unroll
-        for (int k = 0; k < V; ++k) dot += g[c + k] * ev[k];
+        for (int k = 0; k < V; ++k) dot += gv[k] * ev[k];
     }
     dot = wave_sum(dot);
     const float rr = r0[row];
     const float coef = rr * rr * rr * dot / (float)D;
     float* o = de + row * D;
     for (int c = lane * V; c < D; c += kWave * V) {
-        float ev[V];
+        float ev[V], gv[V];
         ld_vec<T>(e + c, ev);
+        ld_vec<T>(g + c, gv);
 #pragma unroll
-        for (int k = 0; k < V; ++k) o[c + k] = rr * g[c + k] - coef * ev[k];
+        for (int k = 0; k < V; ++k) o[c + k] = rr * gv[k] - coef * ev[k];
     }
 }
 
@@ -228,32 +230,32 @@ __device__ __forceinline__ float tanh_r(float y2) {
     return __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(y2) + 1.f);
 }
 
-// One wave per row.  The row's x, dn and residual gradient are read once into
-// registers (MAXC 16-byte chunks of x and dn per lane, and the matching fp32
-// values of dres), all requested before the row's dot product, so a row costs
-// one round trip to HBM and HBM sees each input byte once.
+// One wave per row.  The row's x, dn and residual gradient (all in the
+// storage type T) are read once into registers (MAXC 16-byte chunks of each
+// per lane), all requested before the row's dot product, so a row costs one
+// round trip to HBM and HBM sees each input byte once.  The residual
+// gradient is updated in place: dres <- dres + g - coef x, rounded to T once
+// per norm.  With has_res = 0 (the final norm, where the residual gradient
+// starts) dres is written without being read.
 template <typename T, int MAXC>
 __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     const T* __restrict__ dn, const T* __restrict__ x,
-    const float* __restrict__ r, int N, int D, float* __restrict__ dres,
-    T* __restrict__ dres_t) {
+    const float* __restrict__ r, int N, int D, T* __restrict__ dres, int has_res) {
     constexpr int V = Elt<T>::kVec;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
     if (row >= N) return;
     const T* g = dn + row * D;
     const T* xr = x + row * D;
-    float* d = dres + row * D;
-    uint4 xraw[MAXC], graw[MAXC];
-    float dv[MAXC][V];
+    T* d = dres + row * D;
+    uint4 xraw[MAXC], graw[MAXC], draw[MAXC];
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int c = (ci * kWave + lane) * V;
         if (c < D) {
             xraw[ci] = *reinterpret_cast<const uint4*>(xr + c);
             graw[ci] = *reinterpret_cast<const uint4*>(g + c);
-#pragma unroll
-            for (int k = 0; k < V; ++k) dv[ci][k] = d[c + k];
+            draw[ci] = has_res ? *reinterpret_cast<const uint4*>(d + c) : make_uint4(0, 0, 0, 0);
         }
     }
     float dot = 0.f;
@@ -271,19 +273,17 @@ __global__ __launch_bounds__(kRowThreads) void k_norm_bwd_resid(
     dot = wave_sum(dot);
     const float rr = r[row];
     const float coef = rr * rr * dot / (float)D;
-    T* dt = dres_t + row * D;
 #pragma unroll
     for (int ci = 0; ci < MAXC; ++ci) {
         const int c = (ci * kWave + lane) * V;
         if (c < D) {
-            float xv[V], gv[V], o[V];
+            float xv[V], gv[V], dv[V], o[V];
             unpack_chunk<T>(xraw[ci], xv);
             unpack_chunk<T>(graw[ci], gv);
+            unpack_chunk<T>(draw[ci], dv);
 #pragma unroll
-            for (int k = 0; k < V; ++k) o[k] = dv[ci][k] + gv[k] - coef * xv[k];
-#pragma unroll
-            for (int k = 0; k < V; ++k) d[c + k] = o[k];
-            st_vec<T>(dt + c, o);
+            for (int k = 0; k < V; ++k) o[k] = dv[k] + gv[k] - coef * xv[k];
+            st_vec<T>(d + c, o);
         }
     }
 }
@@ -517,14 +517,15 @@ hipError_t rope_qknorm_bwd(const T* qkv, const float* dq, const float* dk, const
 }
 
 template <typename T>
-hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D,
-                          float* dres, T* dres_t, hipStream_t s) {
+hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D, T* dres,
+                          bool has_res, hipStream_t s) {
     constexpr int VEC = Elt<T>::kVec;
     const int chunks = (int)ceil_div(D, kWave * VEC);
+    const int hr = has_res ? 1 : 0;
 #define NC_NB_CASE(C)                                                                         \
     if (chunks <= C) {                                                                        \
         hipLaunchKernelGGL((k_norm_bwd_resid<T, C>), dim3(row_blocks(N)), dim3(kRowThreads), 0, \
-                           s, dn, x, r, N, D, dres, dres_t);                                  \
+                           s, dn, x, r, N, D, dres, hr);                                      \
         return hipGetLastError();                                                             \
     }
     NC_NB_CASE(1)
@@ -538,7 +539,7 @@ hipError_t norm_bwd_resid(const T* dn, const T* x, const float* r, int N, int D,
 }
 
 template <typename T>
-hipError_t embed_bwd_rows(const float* dh, const T* wte, const int32_t* tok, const float* r0,
+hipError_t embed_bwd_rows(const T* dh, const T* wte, const int32_t* tok, const float* r0,
                           int N, int D, float* de, hipStream_t s) {
     hipLaunchKernelGGL(k_embed_bwd_rows<T>, dim3(row_blocks(N)), dim3(kRowThreads), 0, s, dh,
                        wte, tok, r0, N, D, de);
@@ -614,10 +615,10 @@ hipError_t count_bad_ids(const int32_t* a, const int32_t* b, int64_t n, int V, i
     template hipError_t rope_qknorm_bwd<T>(const T*, const float*, const float*, const float*, \
                                            const float*, const float*, int, int, int, int,     \
                                            const float*, const float*, T*, hipStream_t);       \
-    template hipError_t norm_bwd_resid<T>(const T*, const T*, const float*, int, int,     \
-                                          float*, T*, hipStream_t);                            \
-    template hipError_t embed_bwd_rows<T>(const float*, const T*, const int32_t*,             \
-                                          const float*, int, int, float*, hipStream_t);        \
+    template hipError_t norm_bwd_resid<T>(const T*, const T*, const float*, int, int, T*,  \
+                                          bool, hipStream_t);                                  \
+    template hipError_t embed_bwd_rows<T>(const T*, const T*, const int32_t*, const float*,   \
+                                          int, int, float*, hipStream_t);                      \
     template hipError_t softcap_ce<T>(T*, int64_t, int, int, const int32_t*, float,           \
                                       const float*, float, float*, bool, hipStream_t);         \
     template hipError_t transpose<T>(const T*, int, int, int64_t, T*, int64_t, hipStream_t);  \

@@ -105,7 +105,7 @@ struct Plan {
     size_t bytes = 0;
     // offsets (bytes) of each region inside the workspace
     size_t cos_t, sin_t, r0, x, r1, qkv, rqk, o, lse, xm, r2, g, rf, z, tok_loss, loss_tmp;
-    size_t dres, dres_t, dn, dgu, dout, delta, dq, dk, dv, dqkv, wt, splitk, embed;
+    size_t dres_t, dn, dgu, dout, delta, dq, dk, dv, dqkv, wt, splitk, embed;
     size_t splitk_bytes = 0, embed_bytes = 0;
     int slots = 1;     // saved-activation slots per layer tensor (L with backward, 1 without
                        // or with recompute)
@@ -154,7 +154,6 @@ Plan make_plan(const nc_config& c, bool bwd, bool recompute = false, bool infer 
     p.tok_loss = take(infer ? 0 : (size_t)N * 4);
     p.loss_tmp = take(16);
     if (bwd) {
-        p.dres = take((size_t)N * D * 4);
         p.dres_t = take((size_t)N * D * es);
         p.dn = take((size_t)N * D * 4);
         p.dgu = take((size_t)N * F * es);
@@ -427,15 +426,16 @@ struct Step {
         T* wt = at<T>(p.wt);
         float* sk = at<float>(p.splitk);
         const size_t skb = p.splitk_bytes;
-        float* dres = at<float>(p.dres);
+        // the residual-stream gradient, in the storage type (updated in place
+        // by each norm backward, read by the products as their dY operand)
         T* dres_t = at<T>(p.dres_t);
         // data gradient entering a norm backward, stored as T (the buffer
         // keeps fp32 size: the embedding backward reuses it as fp32 de)
         T* dn = at<T>(p.dn);
         T* z = at<T>(p.z);  // now holds r_f/N * dloss/dz
         auto G_of = [&](int idx) { return grads + lay[idx].offset; };
-        // norm backward with residual: reads dn, x, dres; writes dres, dres_t
-        const double nbb = (double)N * D * (es() + es() + 4 + 4 + es()) + N * 4.0;
+        // norm backward with residual: reads dn, x, dres; writes dres
+        const double nbb = (double)N * D * 4 * es() + N * 4.0;
         auto tb = [&](int64_t r, int64_t k) { return 2.0 * r * k * es(); };
 
         // head: df' = dz' W_lm, dW_lm = dz'^T h_L
@@ -448,9 +448,9 @@ struct Step {
         NC_RUN("gemm_tn_f32", gf(V, D, N), gb(V, D, N, 4.0),
                nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
                            epi(nc::EPI_STORE_F32), sk, skb, s));
-        NC_RUN("zero", 0, N * D * 4.0, nc::zero_elems<float>(dres, N * D, s));
-        NC_RUN("norm_bwd_resid", 0, nbb,
-               nc::norm_bwd_resid<T>(dn, hL, at<float>(p.rf), (int)N, (int)D, dres, dres_t, s));
+        // the residual gradient starts here: written, not read
+        NC_RUN("norm_bwd_resid", 0, nbb - (double)N * D * es(),
+               nc::norm_bwd_resid<T>(dn, hL, at<float>(p.rf), (int)N, (int)D, dres_t, false, s));
 
         T* dgu = at<T>(p.dgu);
         T* dout = at<T>(p.dout);
@@ -484,7 +484,7 @@ struct Step {
                    nc::gemm<T>((int)F, (int)D, (int)N, dgu, F, false, xm, D, false,
                                G_of(i_layer(l, 4)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("norm_bwd_resid", 0, nbb,
-                   nc::norm_bwd_resid<T>(dn, xm, R2(sl), (int)N, (int)D, dres, dres_t, s));
+                   nc::norm_bwd_resid<T>(dn, xm, R2(sl), (int)N, (int)D, dres_t, true, s));
             // attention: xm = x + o W_o^T
             NC_RUN("gemm_nt_store", gf(N, H * hd, D), gb(N, H * hd, D, es()),
                    gemm_w<T>((int)N, (int)(H * hd), (int)D, dres_t, D, W(i_layer(l, 3)), H * hd,
@@ -533,12 +533,12 @@ struct Step {
                    nc::gemm<T>((int)Wq, (int)D, (int)N, dqkv, Wq, false, x, D, false,
                                G_of(i_layer(l, 0)), D, epi(nc::EPI_STORE_F32), sk, skb, s));
             NC_RUN("norm_bwd_resid", 0, nbb,
-                   nc::norm_bwd_resid<T>(dn, x, R1(sl), (int)N, (int)D, dres, dres_t, s));
+                   nc::norm_bwd_resid<T>(dn, x, R1(sl), (int)N, (int)D, dres_t, true, s));
         }
         // embedding: h0 = r0 e, e = W_te[tok]
         float* de = at<float>(p.dn);
-        NC_RUN("embed_bwd_rows", 0, N * D * (4.0 + es() + 4.0),
-               nc::embed_bwd_rows<T>(dres, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de,
+        NC_RUN("embed_bwd_rows", 0, N * D * (es() + es() + 4.0),
+               nc::embed_bwd_rows<T>(dres_t, W(i_wte()), tok, at<float>(p.r0), (int)N, (int)D, de,
                                      s));
         NC_RUN("embed_grad", 0, N * D * 4.0 + (double)V * D * 4.0,
                nc::embed_grad(de, tok, (int)N, (int)D, (int)V, G_of(i_wte()), ws + p.embed,
