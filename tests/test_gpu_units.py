@@ -308,10 +308,12 @@ def test_matmul_epilogue(dtype, mode, M, N, K, b_kmajor):
     auxd = to_dev(auxp, dtype)
     Cd = to_dev(np.full((M, ldc), np.nan, np.float32), dtype)
     rsd = torch.from_numpy(rs).cuda()
-    b.nc_op_matmul_epilogue(DT[dtype], M, N, K, to_dev(A, dtype).data_ptr(), K, True,
+    Ad = to_dev(A, dtype)
+    b.nc_op_matmul_epilogue(DT[dtype], M, N, K, Ad.data_ptr(), K, True,
                             Bd.data_ptr(), ldb, b_kmajor, Cd.data_ptr(), ldc, _EPI[mode],
                             rsd.data_ptr(), auxd.data_ptr(), stream())
     torch.cuda.synchronize()
     got = from_dev(Cd)[:, :N]
     assert np.all(np.isfinite(got))
     assert rel_l2(got, want) < (1e-2 if dtype == "bf16" else 1e-5), (mode, rel_l2(got, want))
+
