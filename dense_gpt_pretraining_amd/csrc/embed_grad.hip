@@ -38,30 +38,78 @@ __global__ __launch_bounds__(kChunk) void k_radix_hist(const int32_t* __restrict
     hist[(int64_t)threadIdx.x * G + blockIdx.x] = h[threadIdx.x];
 }
 
-// in-place exclusive scan of n int32 by one block; writes the total to *total
+// in-place exclusive scan of n int32 by one block; writes the total to *total.
+// The array is taken in tiles of kScanThreads x kScanPer elements: each thread
+// requests its kScanPer consecutive elements at once (four 16-byte loads when
+// they lie inside the array and the array is 16-byte aligned), scans them in
+// registers, and the per-thread sums are scanned across the wave (shuffles)
+// and across the block's waves (one LDS slot per wave).  Integer sums: the
+// result does not depend on the order of the additions.
+constexpr int kScanPer = 16;
 __global__ __launch_bounds__(kScanThreads) void k_exclusive_scan(int32_t* __restrict__ a, int64_t n,
                                                                  int32_t* __restrict__ total) {
-    __shared__ int32_t part[kScanThreads];
-    const int64_t per = (n + kScanThreads - 1) / kScanThreads;
-    const int64_t b = threadIdx.x * per, e = (b + per < n) ? b + per : n;
-    int32_t s = 0;
-    for (int64_t i = b; i < e; ++i) s += a[i];
-    part[threadIdx.x] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan of the per-thread sums
-    for (int off = 1; off < kScanThreads; off <<= 1) {
-        int32_t v = (threadIdx.x >= off) ? part[threadIdx.x - off] : 0;
+    constexpr int kWaves = kScanThreads / 64;
+    __shared__ int32_t wsum[kWaves];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(a) & 15) == 0;
+    int32_t carry = 0;   // sum of every earlier tile
+    for (int64_t base = 0; base < n; base += (int64_t)kScanThreads * kScanPer) {
+        const int64_t i0 = base + (int64_t)t * kScanPer;
+        const bool whole = vec_ok && i0 + kScanPer <= n;
+        int32_t v[kScanPer];
+        if (whole) {
+#pragma unroll
+            for (int q = 0; q < kScanPer / 4; ++q) {
+                const int4 x = reinterpret_cast<const int4*>(a + i0)[q];
+                v[4 * q] = x.x;
+                v[4 * q + 1] = x.y;
+                v[4 * q + 2] = x.z;
+                v[4 * q + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kScanPer; ++k) v[k] = i0 + k < n ? a[i0 + k] : 0;
+        }
+        // exclusive prefix inside the thread; run = the thread's sum
+        int32_t run = 0;
+#pragma unroll
+        for (int k = 0; k < kScanPer; ++k) {
+            const int32_t x = v[k];
+            v[k] = run;
+            run += x;
+        }
+        // inclusive scan of the thread sums across the wave
+        int32_t inc = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += y;
+        }
+        if (lane == 63) wsum[w] = inc;
         __syncthreads();
-        part[threadIdx.x] += v;
-        __syncthreads();
+        int32_t before = 0, tile_sum = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            const int32_t x = wsum[k];
+            before += k < w ? x : 0;
+            tile_sum += x;
+        }
+        const int32_t off = carry + before + inc - run;
+        if (whole) {
+#pragma unroll
+            for (int q = 0; q < kScanPer / 4; ++q)
+                reinterpret_cast<int4*>(a + i0)[q] =
+                    make_int4(v[4 * q] + off, v[4 * q + 1] + off, v[4 * q + 2] + off,
+                              v[4 * q + 3] + off);
+        } else {
+#pragma unroll
+            for (int k = 0; k < kScanPer; ++k)
+                if (i0 + k < n) a[i0 + k] = v[k] + off;
+        }
+        carry += tile_sum;
+        __syncthreads();   // every wave has read wsum before the next tile writes it
     }
-    int32_t run = (threadIdx.x == 0) ? 0 : part[threadIdx.x - 1];
-    for (int64_t i = b; i < e; ++i) {
-        const int32_t v = a[i];
-        a[i] = run;
-        run += v;
-    }
-    if (threadIdx.x == kScanThreads - 1 && total) *total = part[kScanThreads - 1];
+    if (t == 0 && total) *total = carry;
 }
 
 // stable scatter: rank of an element among the earlier elements of its chunk
