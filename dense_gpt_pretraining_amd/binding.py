@@ -124,6 +124,8 @@ _sigs = {
     "nc_op_softcap_ce": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_int64, _P, _P, C.c_float,
                                    _P, C.c_float, _P, C.c_int32, _P]),
     "nc_op_rope_qknorm_fwd": (C.c_int, [C.c_int32] * 5 + [_P, C.c_float, C.c_float, _P, _P, _P]),
+    "nc_op_embedding_grad": (C.c_int, [C.c_int32] * 3 + [_P, _P, _P, _P, C.c_size_t, _P]),
+    "nc_op_embedding_grad_ws_bytes": (C.c_int, [C.c_int32] * 3 + [C.POINTER(C.c_size_t)]),
 }
 for _name, (_res, _args) in _sigs.items():
     _f = getattr(_lib, _name)
@@ -346,6 +348,18 @@ def nc_op_softcap_ce(dtype, N, V, ldz, z, targets, softcap, rowscale, inv_n, tok
 def nc_op_rope_qknorm_fwd(dtype, B, T, H, hd, qkv, base, eps, rqk, tables, stream):
     _check("nc_op_rope_qknorm_fwd", _lib.nc_op_rope_qknorm_fwd(dtype, B, T, H, hd, qkv, base,
                                                                eps, rqk, tables, stream))
+
+
+def nc_op_embedding_grad_ws_bytes(N, D, V) -> int:
+    n = C.c_size_t()
+    _check("nc_op_embedding_grad_ws_bytes",
+           _lib.nc_op_embedding_grad_ws_bytes(N, D, V, C.byref(n)))
+    return n.value
+
+
+def nc_op_embedding_grad(N, D, V, de, tokens, dwte, ws, ws_bytes, stream):
+    _check("nc_op_embedding_grad", _lib.nc_op_embedding_grad(N, D, V, de, tokens, dwte, ws,
+                                                             ws_bytes, stream))
 
 
 def _bf16_bits_rne(w: np.ndarray) -> np.ndarray:

@@ -188,4 +188,25 @@ int nc_op_rope_qknorm_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_
                                                sin_t, eps, rqk, s));
 }
 
+int nc_op_embedding_grad_ws_bytes(int32_t N, int32_t D, int32_t V, size_t* bytes) {
+    if (N < 1 || D < 4 || V < 1 || V > (1 << 24)) return NC_ERR_CONFIG;
+    if (D % 4) return NC_ERR_UNSUPPORTED;
+    if (!bytes) return NC_ERR_NULL;
+    *bytes = nc::embed_grad_ws_bytes(N, D, V);
+    return NC_OK;
+}
+
+int nc_op_embedding_grad(int32_t N, int32_t D, int32_t V, const float* de, const int32_t* tokens,
+                         float* dwte, void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    const int rc = nc_op_embedding_grad_ws_bytes(N, D, V, &need);
+    if (rc != NC_OK) return rc;
+    if (!de || !tokens || !dwte || !ws) return NC_ERR_NULL;
+    if (!al16(de) || !al16(tokens) || !al16(dwte) || (reinterpret_cast<uintptr_t>(ws) & 255))
+        return NC_ERR_ALIGN;
+    if (ws_bytes < need) return NC_ERR_WORKSPACE;
+    hipStream_t s = nc::enqueue_stream(stream);
+    return ret(nc::embed_grad(de, tokens, N, D, V, dwte, ws, ws_bytes, s));
+}
+
 }  // extern "C"

@@ -104,6 +104,22 @@ int nc_op_softcap_ce(int32_t dtype, int32_t N, int32_t V, int64_t ldz, void* z,
 int nc_op_rope_qknorm_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_t hd, void* qkv,
                           float base, float eps, float* rqk, float* tables, void* stream);
 
+/*
+ * Embedding gradient (the backward of the token-embedding lookup, nanochat
+ * article, architecture list): dwte[v] = sum of de[t] over the positions t
+ * with tokens[t] == v.  de fp32 [N, D], tokens int32 [N] with every id in
+ * [0, V), dwte fp32 [V, D], overwritten (rows of ids that do not occur are
+ * 0).  The positions are sorted by id (stable radix sort) and each id's rows
+ * are summed in position order (in pieces of at most 64 rows, whose sums are
+ * then added in order), so the result is bitwise reproducible.  D must be a
+ * multiple of 4.  ws: scratch of at least nc_op_embedding_grad_ws_bytes(N, D,
+ * V) bytes, else NC_ERR_WORKSPACE.  An id outside [0, V) is a precondition
+ * violation that is not checked here (nc_validate_tokens counts them).
+ */
+int nc_op_embedding_grad(int32_t N, int32_t D, int32_t V, const float* de, const int32_t* tokens,
+                         float* dwte, void* ws, size_t ws_bytes, void* stream);
+int nc_op_embedding_grad_ws_bytes(int32_t N, int32_t D, int32_t V, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

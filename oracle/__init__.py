@@ -8,6 +8,7 @@ The GPU library never imports, links or calls anything here.
 from .model import (
     causal_mqa_attention,
     causal_mqa_attention_backward,
+    embedding_gradient,
     forward_backward,
     forward_logits,
     forward_loss,
@@ -21,7 +22,7 @@ from .model import (
 )
 
 __all__ = [
-    "causal_mqa_attention", "causal_mqa_attention_backward",
+    "causal_mqa_attention", "causal_mqa_attention_backward", "embedding_gradient",
     "forward_backward", "forward_logits", "forward_loss", "rms_norm", "rms_norm_backward",
     "rotary", "rotary_backward", "rotary_tables", "softcap",
     "softcap_cross_entropy",

@@ -294,6 +294,16 @@ def _embed(cfg, params, tokens):
     return e, h0, r0
 
 
+def embedding_gradient(tokens: np.ndarray, de: np.ndarray, vocab: int):
+    """dW_te: row v is the sum of de_t over the positions t whose token is v
+    (the embedding lookup's backward; a row no token uses is zero).  tokens
+    int [...], de [..., D]; float64 [vocab, D]."""
+    de = np.asarray(de, dtype=F64)
+    dwte = np.zeros((vocab, de.shape[-1]), dtype=F64)
+    np.add.at(dwte, np.asarray(tokens).reshape(-1), de.reshape(-1, de.shape[-1]))
+    return dwte
+
+
 def _head_loss(cfg, params, h, targets, want_grad):
     """Final norm, untied unembedding, softcap and cross-entropy.
 
@@ -363,9 +373,7 @@ def forward_backward(cfg: dict, params: dict, tokens: np.ndarray,
                              grads)
         inputs[layer] = None
     de = rms_norm_backward(dh, h0, r0)
-    dwte = np.zeros(params["wte"].shape, dtype=F64)
-    np.add.at(dwte, tokens.reshape(-1), de.reshape(-1, de.shape[-1]))
-    grads["wte"] = dwte
+    grads["wte"] = embedding_gradient(tokens, de, params["wte"].shape[0])
     return float(np.mean(tok_loss)), grads
 
 

@@ -206,6 +206,29 @@ def test_ops_validation():
         assert ei.value.code == -7
 
 
+def test_embedding_grad_validation_before_device_work():
+    """Shape, pointer, alignment and workspace checks of the embedding
+    gradient entry point, all before any device work."""
+    b = _b()
+    need = b.nc_op_embedding_grad_ws_bytes(1000, 132, 700)
+    assert need > 0
+    assert b.nc_op_embedding_grad_ws_bytes(2000, 132, 700) > need   # grows with N
+    cases = [
+        ((0, 132, 700, 0x1000, 0x2000, 0x3000, 0x10000, need), -2),       # N < 1: config
+        ((1000, 130, 700, 0x1000, 0x2000, 0x3000, 0x10000, need), -7),    # D % 4: unsupported
+        ((1000, 132, 0, 0x1000, 0x2000, 0x3000, 0x10000, need), -2),      # V < 1
+        ((1000, 132, 700, 0, 0x2000, 0x3000, 0x10000, need), -1),         # null de
+        ((1000, 132, 700, 0x1000, 0x2000, 0x3000, 0, need), -1),          # null workspace
+        ((1000, 132, 700, 0x1004, 0x2000, 0x3000, 0x10000, need), -5),    # de not 16-aligned
+        ((1000, 132, 700, 0x1000, 0x2000, 0x3000, 0x10010, need), -5),    # ws not 256-aligned
+        ((1000, 132, 700, 0x1000, 0x2000, 0x3000, 0x10000, need - 1), -4),  # ws too small
+    ]
+    for args, code in cases:
+        with pytest.raises(b.NcError) as ei:
+            b.nc_op_embedding_grad(*args, None)
+        assert ei.value.code == code, (args, ei.value.code)
+
+
 def test_matmul_epilogue_validation_before_device_work():
     """Every argument check of the fused-epilogue product fails before a launch,
     so none of these fake addresses is ever dereferenced."""

@@ -317,3 +317,75 @@ def test_matmul_epilogue(dtype, mode, M, N, K, b_kmajor):
     assert np.all(np.isfinite(got))
     assert rel_l2(got, want) < (1e-2 if dtype == "bf16" else 1e-5), (mode, rel_l2(got, want))
 
+
+
+def _embedding_grad(N, D, V, de, tok, calls=1):
+    """nc_op_embedding_grad on host arrays; every call writes a NaN-filled
+    output, which the op must overwrite completely."""
+    torch = require_gpu()
+    b = _b()
+    need = b.nc_op_embedding_grad_ws_bytes(N, D, V)
+    ws = torch.empty(need // 4 + 1, dtype=torch.float32, device="cuda")
+    de_d = torch.from_numpy(np.ascontiguousarray(de, dtype=np.float32)).cuda()
+    tok_d = torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32).reshape(-1)).cuda()
+    outs = []
+    for _ in range(calls):
+        out = torch.full((V, D), float("nan"), dtype=torch.float32, device="cuda")
+        b.nc_op_embedding_grad(N, D, V, de_d.data_ptr(), tok_d.data_ptr(), out.data_ptr(),
+                               ws.data_ptr(), need, stream())
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    return outs
+
+
+def test_embedding_gradient_full_size_exact():
+    """The d20 shape (65536 Zipf(1.1) tokens, V = 65536, D = 1280) with
+    integer-valued de in [-8, 8]: every partial sum is an integer below 2^24,
+    so the fp32 sums are exact in any order and the result must equal the
+    oracle's float64 scatter-add bit for bit -- which pins the sort, the cut
+    into pieces and their combination (index work), whatever the order."""
+    from nc_synth import get_config, make_tokens
+    cfg = get_config("d20")
+    tok = make_tokens(cfg)[0].reshape(-1)
+    N, D, V = tok.size, cfg["d_model"], cfg["vocab"]
+    de = np.random.default_rng(11).integers(-8, 9, (N, D)).astype(np.float32)
+    (got,) = _embedding_grad(N, D, V, de, tok)
+    want = oracle.embedding_gradient(tok, de, V)
+    assert np.abs(want).max() < 2 ** 24
+    counts = np.bincount(tok, minlength=V)
+    print(f"[embedding gradient d20] ids used {np.count_nonzero(counts)}, most frequent id "
+          f"{counts.max()} positions ({counts.max() // 64 + 1} pieces)")
+    assert np.array_equal(got, want.astype(np.float32))
+
+
+@pytest.mark.parametrize("N,D,V,kind", [
+    (1000, 132, 700, "uniform"),      # ragged N (not a multiple of 64 or 256), D not of 128
+    (1, 4, 1, "uniform"),             # one position, one id
+    (300, 8, 5, "one id"),            # a single id over 5 pieces of 64 (piece combination)
+    (4099, 64, 65536, "top ids"),     # ids near V - 1: every radix digit non-zero
+    (4096, 1280, 65536, "zipf"),      # a d20 row width, heavy head
+])
+def test_embedding_gradient_bound_and_determinism(N, D, V, kind):
+    """Random de: every element within the fp32 summation bound of the
+    float64 oracle, (n_v - 1) 2^-24 sum |de| for an id used n_v times, rows of
+    unused ids exactly 0, and two calls bitwise equal."""
+    rng = np.random.default_rng(N + V)
+    if kind == "uniform":
+        tok = rng.integers(0, V, N)
+    elif kind == "one id":
+        tok = np.full(N, 3)
+    elif kind == "top ids":
+        tok = V - 1 - rng.integers(0, 50, N)
+    else:
+        from nc_synth.generators import zipf_probs
+        tok = rng.choice(V, size=N, p=zipf_probs(V, 1.1))
+    de = rng.standard_normal((N, D)).astype(np.float32)
+    got, again = _embedding_grad(N, D, V, de, tok, calls=2)
+    want = oracle.embedding_gradient(tok, de, V)
+    counts = np.bincount(tok, minlength=V).astype(np.float64)
+    abs_sum = oracle.embedding_gradient(tok, np.abs(de), V)
+    bound = (np.maximum(counts - 1, 0) * 2.0 ** -24 * 1.01)[:, None] * abs_sum
+    err = np.abs(got.astype(np.float64) - want)
+    assert (err <= bound).all(), float((err - bound).max())
+    assert not got[counts == 0].any()
+    assert np.array_equal(got, again)

@@ -187,6 +187,27 @@ def test_attention_query_chunking_is_exact(monkeypatch):
 
 
 # ----------------------------------------------------------------- softcap / CE
+def test_embedding_gradient_matches_one_hot_product_and_torch():
+    """dW_te of the lookup e_t = W_te[x_t]: the same as the product
+    onehot(x)^T de (a matmul, another route to the same sum) and as torch
+    autograd through an embedding lookup; ids no token uses get zero rows,
+    and the column sums equal those of de."""
+    rng = np.random.default_rng(5)
+    V, D = 37, 6
+    tok = rng.integers(0, 30, (3, 11))          # ids 30..36 never occur
+    tok[0, :5] = 7                              # one id several times
+    de = rng.standard_normal((3, 11, D))
+    got = oracle.embedding_gradient(tok, de, V)
+    onehot = np.zeros((tok.size, V))
+    onehot[np.arange(tok.size), tok.reshape(-1)] = 1.0
+    np.testing.assert_allclose(got, onehot.T @ de.reshape(-1, D), rtol=0, atol=1e-13)
+    w = torch.zeros(V, D, dtype=torch.float64, requires_grad=True)
+    F.embedding(torch.from_numpy(tok), w).backward(torch.from_numpy(de))
+    np.testing.assert_allclose(got, w.grad.numpy(), rtol=0, atol=1e-13)
+    assert not got[30:].any()
+    np.testing.assert_allclose(got.sum(0), de.reshape(-1, D).sum(0), rtol=1e-13, atol=1e-13)
+
+
 def test_softcap_bound_and_series():
     s = 15.0
     z = np.linspace(-500, 500, 10001)
