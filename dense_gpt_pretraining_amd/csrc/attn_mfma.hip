@@ -558,12 +558,19 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
             // their products; the fence keeps the previous block's transpose
             // reads out of that schedule
             __builtin_amdgcn_sched_barrier(0);
+            // A wave issuing matrix products runs at raised priority, so the
+            // other wave of its SIMD (another workgroup's here), when in its
+            // softmax, fills the gaps between products instead of delaying
+            // them; the two waves drift out of phase, and their vector and
+            // matrix work overlap more.
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
                 s = mfma32(lds_b128(sK + (rb0 + row_off[kk])), qf[kk], s);
                 dp = mfma32(lds_b128(sV + (rb0 + row_off[kk])), df[kk], dp);
             }
             sched_reads_ahead<HD / 16, 3, 2, 2>();
+            __builtin_amdgcn_s_setprio(0);
             // keys past the row's position get the score -inf (p = 2^-inf = 0),
             // in a loop of its own so that tiles off the diagonal branch past it
             if (diag) {
@@ -579,6 +586,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
                 const float p = ex2(fmaf(s[rr], scale_log2, nl2));
                 ds[rr] = p * dp[rr];
             }
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const bf16x8_t bd = pack8(&ds[8 * h]);
@@ -588,6 +596,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_mfma(
                     acc[db] = mfma32(lds_tr_frag(sK + (kt + tr_off[db][0]), sK + (kt + tr_off[db][1])),
                                      bd, acc[db]);
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
     for (int it = 0; it < n_tiles; it += 2) {
@@ -835,11 +844,15 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
             const char* dr = sD + qb * 32 * HD * 2;
             const char* vr = sV + wk * 32 * HD * 2;
             f32x16_t s = zero16(), dp = zero16();
+            // matrix products at raised priority, as in the dQ kernel (the
+            // other wave of the SIMD is this workgroup's other row half)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kk = 0; kk < HD / 16; ++kk) {
                 s = mfma32(lds_b128(qr + row_off(kk)), kf[kk], s);
                 dp = mfma32(lds_b128(dr + row_off(kk)), lds_b128(vr + row_off(kk)), dp);
             }
+            __builtin_amdgcn_s_setprio(0);
             // lane holds key `key`; register rr holds row rb0 + 8(rr/4) + 4g + rr%4.
             // Rows before the key's position get the score -inf (p = 2^-inf =
             // 0), in a loop of its own so that blocks every row of which sees
@@ -874,6 +887,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
                 const bf16x8_t bd = pack8(ds);
                 const char* dt = dr + 16 * h * HD * 2;
                 const char* qt = qr + 16 * h * HD * 2;
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int db = 0; db < HD / 32; ++db) {
                     dva[db] = mfma32(lds_tr_frag(dt + tr_off(db, 0), dt + tr_off(db, 1)), bp,
@@ -881,6 +895,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv_mfma(
                     dka[db] = mfma32(lds_tr_frag(qt + tr_off(db, 0), qt + tr_off(db, 1)), bd,
                                      dka[db]);
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
         }
     }
