@@ -113,8 +113,9 @@ int nc_op_rope_qknorm_fwd(int32_t dtype, int32_t B, int32_t T, int32_t H, int32_
  * are summed in position order (in pieces of at most 64 rows, whose sums are
  * then added in order), so the result is bitwise reproducible.  D must be a
  * multiple of 4.  ws: scratch of at least nc_op_embedding_grad_ws_bytes(N, D,
- * V) bytes, else NC_ERR_WORKSPACE.  An id outside [0, V) is a precondition
- * violation that is not checked here (nc_validate_tokens counts them).
+ * V) bytes (else NC_ERR_WORKSPACE), 256-byte aligned (else NC_ERR_ALIGN).  An
+ * id outside [0, V) is a precondition violation that is not checked here
+ * (nc_validate_tokens counts them).
  */
 int nc_op_embedding_grad(int32_t N, int32_t D, int32_t V, const float* de, const int32_t* tokens,
                          float* dwte, void* ws, size_t ws_bytes, void* stream);
