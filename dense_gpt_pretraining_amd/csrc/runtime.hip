@@ -163,9 +163,10 @@ Plan make_plan(const nc_config& c, bool bwd, bool recompute = false, bool infer 
         p.dk = take((size_t)N * hd * 4);
         p.dv = take((size_t)N * hd * 4);
         p.dqkv = take((size_t)N * Wq * es);
-        // the unembedding weight transposed to [D][Vp] (the per-layer data
-        // gradients read their weights where they are stored)
-        p.wt = take((size_t)(D * Vp) * es);
+        // the unembedding weight transposed to [D][Vp] with zero padding, for
+        // a padded vocabulary only (otherwise the head's data gradient reads
+        // W_lm where it is stored, as the per-layer data gradients do)
+        p.wt = take(V == Vp ? 0 : (size_t)(D * Vp) * es);
         size_t sk = 0;
         sk = std::max(sk, nc::gemm_splitk_bytes((int)V, (int)D, (int)N));
         sk = std::max(sk, nc::gemm_splitk_bytes((int)D, (int)F, (int)N));
@@ -440,11 +441,18 @@ struct Step {
 
         // head: df' = dz' W_lm, dW_lm = dz'^T h_L
         T* hL = X(L);
-        NC_RUN("transpose_w", 0, tb(V, D),
-               nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
-        NC_RUN("gemm_nt_dn", gf(N, D, V), gb(N, D, V, es()),
-               nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
-                           epi(nc::EPI_STORE_T), nullptr, 0, s));
+        if (V == Vp) {
+            // no padded columns: the product reads W_lm where it is stored
+            NC_RUN("gemm_nt_dn", gf(N, D, V), gb(N, D, V, es()),
+                   gemm_w<T>((int)N, (int)D, (int)V, z, Vp, W(i_wlm()), D, dn, D,
+                             epi(nc::EPI_STORE_T), s));
+        } else {
+            NC_RUN("transpose_w", 0, tb(V, D),
+                   nc::transpose<T>(W(i_wlm()), (int)V, (int)D, D, wt, Vp, s));
+            NC_RUN("gemm_nt_dn", gf(N, D, V), gb(N, D, V, es()),
+                   nc::gemm<T>((int)N, (int)D, (int)Vp, z, Vp, true, wt, Vp, true, dn, D,
+                               epi(nc::EPI_STORE_T), nullptr, 0, s));
+        }
         NC_RUN("gemm_tn_f32", gf(V, D, N), gb(V, D, N, 4.0),
                nc::gemm<T>((int)V, (int)D, (int)N, z, Vp, false, hL, D, false, G_of(i_wlm()), D,
                            epi(nc::EPI_STORE_F32), sk, skb, s));
